@@ -1,0 +1,417 @@
+"""Pins for the FP64 CPU oracle, each against something other than the oracle itself.
+
+The pages print no attention values for a worked example, so the oracle is
+pinned by: a library routine the cases reduce to (torch's
+``scaled_dot_product_attention`` in float64 on the CPU with an explicit
+additive mask and its own GQA repeat; Hugging Face's Llama rotate-half RoPE,
+the non-interleaved convention candle's ``rope`` uses), closed forms (uniform
+weights over a known index range recover that range's first two moments), the
+invariants the ffai-argus text.rs page argues (a skipped column equals a -inf
+column bit for bit; the GQA fold equals repeat_kv; a decode step sees the
+whole cache; causal rows sum to one with an exactly zero tail) and exact
+values (the first RoPE frequency is exactly 1, so its table is libm's cos/sin
+of the integer position).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_attention_varlen_amd import workloads as wl
+
+D = 64
+
+
+# ----------------------------------------------------------------------------- RoPE tables
+
+@pytest.mark.parametrize("theta", [10000.0, 100000.0, 160000.0])
+def test_rope_table_position_zero_is_identity(theta):
+    cos, sin = oracle.rope_tables(theta, 4)
+    assert np.all(cos[0] == 1.0) and np.all(sin[0] == 0.0)
+
+
+def test_rope_table_first_frequency_is_exact():
+    # theta^0 = 1, so the first pair's angle is the integer position itself.
+    cos, sin = oracle.rope_tables(160000.0, 8192)
+    for p in [0, 1, 2, 3, 7, 100, 1142, 4095, 8191]:
+        assert cos[p, 0] == np.float32(math.cos(p))
+        assert sin[p, 0] == np.float32(math.sin(p))
+
+
+@pytest.mark.parametrize("theta", [10000.0, 100000.0, 160000.0])
+def test_rope_table_within_f32_angle_rounding(theta):
+    # Against the exact angle p * theta^(-i/32): the table's angle carries at most
+    # three f32 roundings (theta^e, 1/x, p*inv), each <= 2^-24 relative, and the
+    # stored cos/sin one more 2^-25 absolute.
+    L = 8192
+    cos, sin = oracle.rope_tables(theta, L)
+    p = np.arange(L, dtype=np.float64)[:, None]
+    i = np.arange(32, dtype=np.float64)[None, :]
+    ang = p * theta ** (-i / 32.0)
+    bound = 3.0 * 2.0 ** -24 * ang + 2.0 ** -24 + 1e-12
+    assert np.all(np.abs(cos - np.cos(ang)) <= bound)
+    assert np.all(np.abs(sin - np.sin(ang)) <= bound)
+    # and a plausible mistake -- the exponent i/64 instead of 2i/64 -- is far outside it
+    wrong = p * theta ** (-i / 64.0)
+    assert np.max(np.abs(cos - np.cos(wrong))) > 0.1
+
+
+# ----------------------------------------------------------------------------- RoPE rotation
+
+def _hf_rope(x64, pos, cos, sin):
+    """Hugging Face Llama rotate-half RoPE (library routine) on (T, heads, 64) float64."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    c = torch.from_numpy(np.concatenate([cos[pos], cos[pos]], -1).astype(np.float64))
+    s = torch.from_numpy(np.concatenate([sin[pos], sin[pos]], -1).astype(np.float64))
+    xt = torch.from_numpy(x64).transpose(0, 1)[None]        # (1, heads, T, 64)
+    y, _ = apply_rotary_pos_emb(xt, xt, c[None], s[None], unsqueeze_dim=1)
+    return y[0].transpose(0, 1).numpy()
+
+
+def test_rope_matches_library_rotate_half():
+    rng = np.random.default_rng(7)
+    T, heads = 300, 5
+    x = rng.standard_normal((T, heads * D), dtype=np.float32)
+    pos = rng.integers(0, 8192, T).astype(np.int32)
+    cos, sin = oracle.rope_tables(100000.0, 8192)
+    ours = oracle.rope_apply(x, heads, pos, cos, sin).reshape(T, heads, D)
+    ref = _hf_rope(x.astype(np.float64).reshape(T, heads, D), pos, cos, sin)
+    # ours is the f64 rotation rounded once to f32: within half an f32 ulp
+    assert np.all(np.abs(ours - ref) <= np.abs(ref) * 2.0 ** -24 + 1e-30)
+
+
+def test_rope_preserves_pair_norms_and_keeps_zero():
+    rng = np.random.default_rng(8)
+    T = 64
+    x = rng.standard_normal((T, D), dtype=np.float32)
+    pos = np.arange(T, dtype=np.int32) * 97
+    cos, sin = oracle.rope_tables(10000.0, 8192)
+    y = oracle.rope_apply(x, 1, pos, cos, sin).astype(np.float64)
+    n_in = x[:, :32].astype(np.float64) ** 2 + x[:, 32:].astype(np.float64) ** 2
+    n_out = y[:, :32] ** 2 + y[:, 32:] ** 2
+    unit = cos[pos].astype(np.float64) ** 2 + sin[pos].astype(np.float64) ** 2
+    assert np.allclose(n_out, n_in * unit, rtol=1e-6, atol=1e-6)
+    z = oracle.rope_apply(np.zeros((T, D), np.float32), 1, pos, cos, sin)
+    assert np.all(z == 0.0)
+
+
+# ----------------------------------------------------------------------------- attention vs library
+
+def _sdpa_reference(case, tables=None):
+    """torch SDPA (float64, CPU) per sequence with an explicit additive mask and its GQA repeat."""
+    H, G = case.H, case.G
+    out = np.zeros((case.T, H * D), np.float64)
+    for s in range(case.S):
+        lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        q = case.q[lo:hi].astype(np.float64).reshape(n, H, D)
+        k = case.k[lo:hi].astype(np.float64).reshape(n, G, D)
+        v = case.v[lo:hi].astype(np.float64).reshape(n, G, D)
+        if tables is not None:
+            pos = np.arange(n)
+            q = _hf_rope(q, pos, *tables)
+            k = _hf_rope(k, pos, *tables)
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        ok = np.ones((n, n), bool)
+        if case.window >= 0:
+            ok &= np.abs(i - j) <= case.window // 2
+        if case.causal:
+            ok &= j <= i
+        mask = torch.from_numpy(np.where(ok, 0.0, -np.inf))
+        qt = torch.from_numpy(q).transpose(0, 1)[None]
+        kt = torch.from_numpy(np.ascontiguousarray(k)).transpose(0, 1)[None].contiguous()
+        vt = torch.from_numpy(np.ascontiguousarray(v)).transpose(0, 1)[None].contiguous()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt.contiguous(), kt, vt, attn_mask=mask, scale=0.125, enable_gqa=(H != G))
+        out[lo:hi] = o[0].transpose(0, 1).reshape(n, H * D).numpy()
+    return out
+
+
+SMALL_MASKS = [(-1, False), (-1, True), (0, False), (1, False), (2, False), (3, True),
+               (4, False), (7, False), (9, True), (16, False)]
+
+
+@pytest.mark.parametrize("window,causal", SMALL_MASKS)
+@pytest.mark.parametrize("H,G", [(4, 4), (4, 2), (6, 2), (3, 1)])
+def test_attention_matches_library_on_tiny_inputs(window, causal, H, G):
+    case = wl.make_prefill([1, 2, 5, 8, 0, 3], H, G, packed=(H == G), window=window,
+                           causal=causal, seed=11 + H + G)
+    ours = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, window, causal)
+    ref = _sdpa_reference(case)
+    assert np.all(np.abs(ours - ref) <= np.abs(ref) * 2.0 ** -23 + 1e-12)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (6, False), (5, True)])
+def test_attention_with_rope_matches_library(window, causal):
+    case = wl.make_prefill([13, 1, 30], 6, 2, packed=False, window=window, causal=causal,
+                           theta=100000.0, seed=5)
+    tables = oracle.rope_tables(case.theta, 64)
+    ours = oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, window,
+                                   causal, tables=tables)
+    ref = _sdpa_reference(case, tables)
+    assert np.all(np.abs(ours - ref) <= np.abs(ref) * 2.0 ** -23 + 1e-12)
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def _moment_case(lengths, H, G, window, causal):
+    """q = 0 (uniform weights), v_j = [1, p_j, p_j^2, 0, ...] with p_j the key's position."""
+    case = wl.make_prefill(lengths, H, G, packed=False, window=window, causal=causal, seed=3)
+    case.q[:] = 0.0
+    case.v[:] = 0.0
+    for s in range(case.S):
+        lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+        p = np.arange(hi - lo, dtype=np.float32)
+        for g in range(G):
+            case.v[lo:hi, g * D + 0] = 1.0
+            case.v[lo:hi, g * D + 1] = p
+            case.v[lo:hi, g * D + 2] = p * p
+    return case
+
+
+def _range_moments(a, b):
+    """Mean and mean square of the integers a..b (closed forms)."""
+    cnt = b - a + 1
+    s1 = (a + b) * cnt / 2.0
+    sq = lambda m: m * (m + 1) * (2 * m + 1) / 6.0
+    s2 = sq(b) - (sq(a - 1) if a > 0 else 0.0)
+    return s1 / cnt, s2 / cnt
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (0, False), (1, False),
+                                           (128, False), (5, False), (7, True), (64, True)])
+def test_uniform_weights_recover_the_visible_range(window, causal):
+    lengths = [1, 37, 91, 130, 2]
+    case = _moment_case(lengths, 4, 2, window, causal)
+    tables = oracle.rope_tables(10000.0, 256)   # rotating q = 0 keeps it 0
+    out = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 2, window, causal,
+                                  tables=tables)
+    h = window // 2 if window >= 0 else 10 ** 9
+    for s in range(case.S):
+        lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+        n = hi - lo
+        for i in range(n):
+            a = max(0, i - h)
+            b = i if causal else min(n - 1, i + h)
+            m1, m2 = _range_moments(a, b)
+            for head in range(4):
+                row = out[lo + i, head * D: head * D + 3].astype(np.float64)
+                assert row[0] == pytest.approx(1.0, abs=1e-7)
+                assert row[1] == pytest.approx(m1, rel=1e-6, abs=1e-6)
+                assert row[2] == pytest.approx(m2, rel=1e-6, abs=1e-6)
+            assert np.all(out[lo + i].reshape(4, D)[:, 3:] == 0.0)
+
+
+@pytest.mark.parametrize("window,causal", SMALL_MASKS)
+def test_rows_sum_to_one(window, causal):
+    case = wl.make_prefill([33, 64, 5], 2, 2, packed=True, window=window, causal=causal, seed=4)
+    case.v[:] = 1.0
+    out = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 2, 2, window, causal)
+    assert np.all(np.abs(out - 1.0) <= 2.0 ** -23)
+
+
+def test_causal_probabilities_through_identity_values():
+    # V = I recovers P: each causal row sums to one and its tail past the limit is exactly 0
+    # (the argus tests on s = 33 with two heads).
+    n, H = 33, 2
+    case = wl.make_prefill([n], H, H, packed=False, causal=True, seed=9)
+    case.q[:] *= 3.0
+    case.v[:] = 0.0
+    for h in range(H):
+        case.v[:, h * D:h * D + n] = np.eye(n, dtype=np.float32)
+    P = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, H, -1, True)
+    for h in range(H):
+        for i in range(n):
+            row = P[i, h * D:h * D + n].astype(np.float64)
+            assert abs(row.sum() - 1.0) < 1e-6
+            assert np.all(row[:i + 1] > 0.0)
+            assert np.all(row[i + 1:] == 0.0)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+ALL_MASKS = SMALL_MASKS + [(128, False), (33, True)]
+
+
+@pytest.mark.parametrize("window,causal", ALL_MASKS)
+def test_skipping_masked_columns_is_bit_identical_to_minus_inf(window, causal):
+    case = wl.make_prefill([40, 1, 77, 12], 4, 2, packed=False, window=window, causal=causal,
+                           seed=21)
+    tables = oracle.rope_tables(10000.0, 128)
+    a = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 2, window, causal,
+                                tables=tables, mask_mode=0)
+    b = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 2, window, causal,
+                                tables=tables, mask_mode=1)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_of_twice_the_length_equals_global(causal):
+    case = wl.make_prefill([50, 17, 90], 4, 4, packed=True, causal=causal, seed=22)
+    tables = oracle.rope_tables(10000.0, 128)
+    glob = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 4, -1, causal,
+                                   tables=tables)
+    wide = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 4, 180, causal,
+                                   tables=tables)
+    assert np.array_equal(glob, wide)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (10, False)])
+def test_gqa_equals_mha_with_repeated_kv(window, causal):
+    H, G = 9, 3
+    case = wl.make_prefill([31, 60], H, G, packed=False, window=window, causal=causal, seed=23)
+    tables = oracle.rope_tables(100000.0, 64)
+    gqa = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, window, causal,
+                                  tables=tables)
+    T = case.T
+    k_rep = np.repeat(case.k.reshape(T, G, 1, D), H // G, axis=2).reshape(T, H * D)
+    v_rep = np.repeat(case.v.reshape(T, G, 1, D), H // G, axis=2).reshape(T, H * D)
+    mha = oracle.varlen_attention(case.q, k_rep, v_rep, case.cu, H, H, window, causal,
+                                  tables=tables)
+    assert np.array_equal(gqa, mha)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (12, False)])
+def test_each_sequence_alone_equals_its_rows_in_the_batch(window, causal):
+    lengths = [20, 0, 45, 7]
+    case = wl.make_prefill(lengths, 4, 4, packed=True, window=window, causal=causal, seed=24)
+    tables = oracle.rope_tables(10000.0, 64)
+    packed = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 4, window, causal,
+                                     tables=tables)
+    for s, n in enumerate(lengths):
+        lo = int(case.cu[s])
+        cu1 = np.array([0, n], np.int32)
+        alone = oracle.varlen_attention(case.q[lo:lo + n], case.k[lo:lo + n], case.v[lo:lo + n],
+                                        cu1, 4, 4, window, causal, tables=tables)
+        assert np.array_equal(alone, packed[lo:lo + n])
+
+
+def test_sampled_rows_equal_full_rows():
+    case = wl.make_prefill([70, 3, 129], 4, 2, packed=False, window=20, causal=False, seed=25)
+    tables = oracle.rope_tables(10000.0, 256)
+    full = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 2, 20, False,
+                                   tables=tables)
+    rows = np.array([0, 69, 70, 72, 73, 201, 100], np.int32)
+    part = oracle.varlen_attention(case.q, case.k, case.v, case.cu, 4, 2, 20, False,
+                                   tables=tables, rows=rows)
+    assert np.array_equal(part, full[rows])
+
+
+# ----------------------------------------------------------------------------- decode
+
+def test_decode_equals_last_causal_row_bitwise_without_rotation():
+    # Unrotated inputs: the decode row over a cache holding the sequence's keys is the last
+    # row of causal prefill on that sequence (argus `CausalSoftmax` with offset L-1).
+    H, G, cap = 9, 3, 96
+    rng = np.random.default_rng(31)
+    lens = [1, 50, 96]
+    B = len(lens)
+    kc = rng.standard_normal((B, G, cap, D), dtype=np.float32)
+    vc = rng.standard_normal((B, G, cap, D), dtype=np.float32)
+    qn = rng.standard_normal((B, H * D), dtype=np.float32)
+    kn = rng.standard_normal((B, G * D), dtype=np.float32)
+    vn = rng.standard_normal((B, G * D), dtype=np.float32)
+    used = np.array(lens, np.int32)
+    out, kc2, vc2 = oracle.decode(qn, kn, vn, kc, vc, used, H, G)
+    for b, L in enumerate(lens):
+        k_seq = kc2[b, :, :L].transpose(1, 0, 2).reshape(L, G * D)
+        v_seq = vc2[b, :, :L].transpose(1, 0, 2).reshape(L, G * D)
+        q_seq = np.zeros((L, H * D), np.float32)
+        q_seq[L - 1] = qn[b]
+        pre = oracle.varlen_attention(q_seq, k_seq, v_seq, np.array([0, L], np.int32), H, G,
+                                      -1, True)
+        assert np.array_equal(pre[L - 1], out[b])
+        # the append wrote row L-1 and nothing else
+        assert np.array_equal(kc2[b, :, L - 1], kn[b].reshape(G, D))
+        assert np.array_equal(vc2[b, :, L - 1], vn[b].reshape(G, D))
+        mask = np.ones(cap, bool)
+        mask[L - 1] = False
+        assert np.array_equal(kc2[b][:, mask], kc[b][:, mask])
+        assert np.array_equal(vc2[b][:, mask], vc[b][:, mask])
+
+
+def test_decode_with_rotation_matches_causal_prefill():
+    H, G, L = 6, 2, 70
+    case = wl.make_prefill([L], H, G, packed=False, causal=True, theta=100000.0, seed=32)
+    tables = oracle.rope_tables(case.theta, 128)
+    pre = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, -1, True,
+                                  tables=tables)
+    cap = 128
+    kc = np.zeros((1, G, cap, D), np.float32)
+    vc = np.zeros((1, G, cap, D), np.float32)
+    pos = np.arange(L - 1, dtype=np.int32)
+    kc[0, :, :L - 1] = oracle.rope_apply(case.k[:L - 1], G, pos, *tables).reshape(
+        L - 1, G, D).transpose(1, 0, 2)
+    vc[0, :, :L - 1] = case.v[:L - 1].reshape(L - 1, G, D).transpose(1, 0, 2)
+    out, kc2, _ = oracle.decode(case.q[L - 1:], case.k[L - 1:], case.v[L - 1:], kc, vc,
+                                np.array([L], np.int32), H, G, tables=tables)
+    # decode scores keys stored in f32; prefill keeps them in f64: a rounding apart
+    assert np.max(np.abs(out[0] - pre[L - 1])) < 1e-6
+    # the appended key is the rotated new key (library rotate-half, f32 rounding)
+    ref = _hf_rope(case.k[L - 1:].astype(np.float64).reshape(1, G, D), np.array([L - 1]),
+                   *tables)
+    assert np.all(np.abs(kc2[0, :, L - 1] - ref[0]) <= np.abs(ref[0]) * 2.0 ** -24 + 1e-30)
+
+
+def test_decode_attends_to_the_entire_cache():
+    # q = 0, v_j = [1, j, j^2]: the output is the mean over 0..L-1, so L is recovered exactly,
+    # appended row included (argus `a_decode_step_attends_to_the_entire_cache`).
+    H, G, cap = 3, 1, 200
+    lens = np.array([1, 2, 40, 199, 200], np.int32)
+    B = len(lens)
+    kc = np.random.default_rng(1).standard_normal((B, G, cap, D), dtype=np.float32)
+    vc = np.zeros((B, G, cap, D), np.float32)
+    j = np.arange(cap, dtype=np.float32)
+    vc[:, :, :, 0] = 1.0
+    vc[:, :, :, 1] = j
+    vc[:, :, :, 2] = j * j
+    qn = np.zeros((B, H * D), np.float32)
+    kn = np.random.default_rng(2).standard_normal((B, G * D), dtype=np.float32)
+    vn = np.zeros((B, G * D), np.float32)
+    vn[:, 0] = 1.0
+    vn[:, 1] = lens - 1
+    vn[:, 2] = (lens - 1.0) ** 2
+    tables = oracle.rope_tables(100000.0, 256)
+    out, _, _ = oracle.decode(qn, kn, vn, kc, vc, lens, H, G, tables=tables)
+    for b, L in enumerate(lens):
+        m1, m2 = _range_moments(0, int(L) - 1)
+        for h in range(H):
+            assert out[b, h * D] == pytest.approx(1.0, abs=1e-7)
+            assert out[b, h * D + 1] == pytest.approx(m1, rel=1e-6, abs=1e-6)
+            assert out[b, h * D + 2] == pytest.approx(m2, rel=1e-6, abs=1e-6)
+
+
+def test_decode_probabilities_all_positive_and_sum_to_one():
+    H, G, cap, L = 2, 2, 40, 40
+    rng = np.random.default_rng(3)
+    kc = rng.standard_normal((1, G, cap, D), dtype=np.float32)
+    vc = np.zeros((1, G, cap, D), np.float32)
+    for g in range(G):
+        vc[0, g, :, :L] = np.eye(L, dtype=np.float32)
+    qn = rng.standard_normal((1, H * D), dtype=np.float32) * 2
+    kn = rng.standard_normal((1, G * D), dtype=np.float32)
+    vn = np.zeros((1, G * D), np.float32)
+    for g in range(G):
+        vn[0, g * D + L - 1] = 1.0
+    out, _, _ = oracle.decode(qn, kn, vn, kc, vc, np.array([L], np.int32), H, G)
+    for h in range(H):
+        p = out[0, h * D:h * D + L].astype(np.float64)
+        assert np.all(p > 0.0)
+        assert abs(p.sum() - 1.0) < 1e-6
+
+
+# ----------------------------------------------------------------------------- argument checks
+
+def test_oracle_rejects_bad_offsets():
+    q = np.zeros((4, D), np.float32)
+    with pytest.raises(ValueError):
+        oracle.varlen_attention(q, q, q, np.array([0, 3, 2, 4], np.int32), 1, 1)
+    with pytest.raises(ValueError):
+        oracle.varlen_attention(q, q, q, np.array([1, 4], np.int32), 1, 1)
+    with pytest.raises(ValueError):
+        oracle.varlen_attention(q, q, q, np.array([0, 4], np.int32), 3, 2)
