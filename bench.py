@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the varlen attention hot path on one MI355X.
+
+Prints ONE JSON line.  A step is one pass of the hot path over the headline
+workload (ModernBERT-base local layer: 64 packed sequences of U[16,512]
+tokens, 12 heads, window 128, RoPE theta 1e4): the RoPE prologue then the
+attention forward, inputs resident in HBM.  The same line carries the other
+workloads of the path, each timed per call with HIP events on the stream it
+runs on and the L2/MALL flushed between calls:
+
+  prefill_global_long   ModernBERT global layer, 8 x U[4096,8192]
+  prefill_causal_1142   SmolLM2 causal GQA prefill, one 1142-token sequence
+  prefill_causal_16x2048 SmolLM2 causal GQA prefill, 16 x 2048
+  decode_b64            SmolLM2 decode, 64 sequences, caches [64][3][8192][64]
+
+`roofline` is for the headline step's dominant kernel (the attention tile
+kernel): algorithmic FLOPs per launch over its mean launch time.  `traffic`
+comes from rocprofv3 PMC counters taken offline (see profiles/), or null.
+`cpu_baseline` times the FP64 CPU oracle on a bounded random sample of the
+headline workload's rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+HEADLINE = "1"
+PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
+         "3b": "prefill_causal_16x2048", "4": "decode_b64"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--parts", default="2,3a,3b,4",
+                    help="comma list of extra workloads to time, or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the CPU oracle baseline (0 disables)")
+    ap.add_argument("--only", default=None,
+                    help="run only this workload's loop (for profiling): 1, 2, 3a, 3b or 4")
+    return ap.parse_args()
+
+
+class Flusher:
+    """Writes a buffer larger than L2 + MALL so the next call starts cold."""
+
+    def __init__(self, torch, nbytes=1 << 30):
+        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def time_calls(torch, fn, steps, warmup, flush=None):
+    """Mean and min ms of `fn` per call with events around each call on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.mean(times)), float(np.min(times))
+
+
+def prefill_part(torch, key, steps, warmup, flush):
+    from transformer_attention_varlen_amd import metrics, workloads as wl
+    from transformer_attention_varlen_amd.session import PrefillRun
+    case = wl.build(key)
+    run = PrefillRun(case)
+    run.rope()
+    mean_ms, min_ms = time_calls(torch, run.attention, steps, warmup, flush)
+    rope_ms, _ = time_calls(torch, run.rope, max(3, steps // 4), 1, flush)
+    flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    rb = metrics.rope_bytes(case.T, case.H, case.G)
+    res = {"workload": wl.WORKLOADS[key].name, "tokens": case.T, "seqs": case.S,
+           "heads": case.H, "kv_heads": case.G, "window": case.window, "causal": case.causal,
+           "attn_ms": round(mean_ms, 4), "attn_ms_min": round(min_ms, 4),
+           "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
+           "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
+           "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+           "rope_ms": round(rope_ms, 4),
+           "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1)}
+    del run
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_part(torch, steps, warmup, flush):
+    from transformer_attention_varlen_amd import metrics, workloads as wl
+    from transformer_attention_varlen_amd.session import DecodeRun
+    case = wl.build("4")
+    run = DecodeRun(case, rotate=True)
+    mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
+    nbytes = metrics.decode_bytes(case.used, case.H, case.G)
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    res = {"workload": wl.WORKLOADS["4"].name, "seqs": case.B, "heads": case.H,
+           "kv_heads": case.G, "cap": case.cap, "sum_used": int(case.used.sum()),
+           "decode_ms": round(mean_ms, 4), "decode_ms_min": round(min_ms, 4),
+           "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
+           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del run
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle, untuned, on a random sample of the workload's rows (all heads each)."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    tables = oracle.rope_tables(case.theta, max(int(case.lengths.max()), 1))
+    rng = np.random.default_rng(0)
+    n = 64
+    spent = 0.0
+    done = 0
+    while True:
+        rows = np.sort(rng.integers(0, case.T, n)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
+                                case.causal, tables=tables, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done += n
+        if spent >= budget_s or done >= case.T:
+            break
+        n = int(min(max(n * 2, 1), max(1, (budget_s - spent) / max(dt / n, 1e-9))))
+    return {"value": round(done / spent / 1e6, 6), "unit": "Mtok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} random query rows (all {case.H} heads, RoPE + -inf mask + two-pass "
+                      f"softmax in FP64) of the headline workload, {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from transformer_attention_varlen_amd import kattn, metrics, workloads as wl
+    from transformer_attention_varlen_amd.session import PrefillRun
+
+    kattn.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.only is not None:
+        # profiling mode: just the named workload's loop, nothing else
+        if args.only == "4":
+            from transformer_attention_varlen_amd.session import DecodeRun
+            run = DecodeRun(wl.build("4"), rotate=True)
+            fn = run.step
+        else:
+            run = PrefillRun(wl.build(args.only))
+            fn = run.step
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup}))
+        return
+
+    case = wl.build(HEADLINE)
+    run = PrefillRun(case)
+    # warmup, then K timed steps bracketed by synchronisation; the attention launch of each
+    # step is also bracketed by events on the stream it is queued on
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        run.rope()
+        a.record()
+        run.attention()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    value = case.T / (ms_per_step * 1e-3) / 1e6
+
+    out = {
+        "metric": "varlen attention Mtok/s + % FP32-MFMA peak; decode KV GB/s (% HBM)",
+        "value": round(value, 3), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.WORKLOADS[HEADLINE].name, "tokens": case.T, "seqs": case.S,
+                   "heads": case.H, "kv_heads": case.G, "head_dim": 64, "window": case.window,
+                   "causal": case.causal, "rope_theta": case.theta,
+                   "seed": wl.WORKLOADS[HEADLINE].seed,
+                   "step": "rope prologue + attention forward"},
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel (attention tile kernel)",
+                     "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": None, "mean_launch_ms": round(attn_ms, 4),
+                     "algorithmic_gflop_per_launch": round(flops / 1e9, 4)},
+    }
+    del run
+    torch.cuda.empty_cache()
+
+    parts = {}
+    keys = [] if args.parts == "none" else [k for k in args.parts.split(",") if k]
+    if keys:
+        flush = Flusher(torch)
+        for k in keys:
+            psteps, pwarm = max(5, args.steps // 2), 2
+            if k == "4":
+                parts[PARTS[k]] = decode_part(torch, psteps, pwarm, flush)
+            else:
+                parts[PARTS[k]] = prefill_part(torch, k, psteps, pwarm, flush)
+        del flush
+    out["parts"] = parts
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * kattn.h -- C ABI of libkattn.so: packed variable-length attention on the
+ * AMD MI355X (gfx950), head width 64, FP32 in and out.
+ *
+ * Sources (docs.rs source pages):
+ *   [kime-cpu plan.rs]   kime-cpu 0.0.17, src/kime_cpu/plan.rs -- CPU backend
+ *   [kime-cuda plan.rs]  kime-cuda 0.0.3, src/plan.rs -- CUDA backend
+ *   [argus text.rs]      ffai-argus 0.7.3, src/text.rs -- SmolLM2 text tower
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Status: KATTN_OK (0) or a negative KATTN_E* code.  On error,
+ *   kattn_last_error() returns a message for the calling thread, valid until
+ *   that thread's next kattn call.  Every argument check runs on the host and
+ *   fails before anything is queued on the device (errors are values, as in
+ *   the kime pages' lowering checks and the argus cache append's bail-outs).
+ * - Pointers marked "device" are device memory owned by the caller (for
+ *   example torch tensors); "host" pointers are host memory owned by the
+ *   caller.  The library keeps no pointer after a call returns and allocates
+ *   no memory on any call.
+ * - Device calls queue work on `stream` (NULL: the null stream) and return
+ *   without synchronising.  Errors raised by the device after the call
+ *   returns show up at the caller's next synchronisation.
+ * - Strides are in floats.  Every float pointer and every stride must be a
+ *   multiple of 16 bytes (4 floats); the kernels load and store 16 bytes at a
+ *   time.
+ * - head_dim must be 64 (the pages lower heads of 64 only).
+ * - Device index tables (cu, pos, used) are preconditions: kattn_build_index
+ *   produces well-formed ones.  The kernels never read or write outside the
+ *   buffers the sizes describe even when a table is malformed (offsets are
+ *   clamped to [0, T], positions outside the table leave a row unrotated),
+ *   but the results are then unspecified.  With KATTN_CHECK=1 in the
+ *   environment each call copies its device tables to the host, validates
+ *   them and returns KATTN_EBOUNDS on a bad one (synchronous; debugging
+ *   only).
+ */
+#ifndef KATTN_H
+#define KATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KATTN_OK = 0,
+    KATTN_EINVAL = -1,       /* null pointer, negative size, bad scalar */
+    KATTN_EUNSUPPORTED = -2, /* head_dim != 64, H % G != 0, misaligned pointer or stride */
+    KATTN_EBOUNDS = -3,      /* offsets, lengths, table or workspace too small */
+    KATTN_EDEVICE = -4       /* a HIP call failed */
+};
+
+/* Message for the last failed call on this thread ("" after a success). */
+const char* kattn_last_error(void);
+
+/*
+ * RoPE cos/sin tables for heads of 64 at one base `theta`, positions
+ * 0..len-1, written to host arrays cos_host[len][32], sin_host[len][32].
+ * Rounding follows [kime-cuda plan.rs] `rope_tables`, which that page states
+ * matches the CPU backend: the exponent 2i/64 in f32, theta^e in f64 rounded
+ * to f32, its f32 reciprocal, the f32 product with the f32 position, and
+ * cos/sin of that angle in f64 rounded to f32.  The caller copies the tables
+ * to the device once per base (the pages deduplicate tables by base).
+ * Errors: EINVAL for theta <= 0 or not finite, len < 0, null outputs.
+ */
+int kattn_rope_tables(double theta, int32_t len, float* cos_host, float* sin_host);
+
+/*
+ * Host index build for a packed batch ([kime-cpu plan.rs] `CpuBackend::run`;
+ * [kime-cuda plan.rs] `CudaBackend::run`): sequence s holds rows
+ * cu[s] .. cu[s+1]-1 of every activation.
+ *   cu_host:  host int32[S+1]; must satisfy cu[0] = 0, cu[s] <= cu[s+1], cu[S] = T.
+ *   seq_host: host int32[T] or NULL; seq[r] = the sequence holding row r.
+ *   pos_host: host int32[T] or NULL; pos[r] = r - cu[seq[r]], the position
+ *             inside the sequence (RoPE restarts at 0 in every sequence).
+ *   max_seqlen_out: host int32* or NULL; the longest sequence.
+ * Errors: EINVAL for S < 0, T < 0 or cu_host NULL; EBOUNDS for malformed cu.
+ */
+int kattn_build_index(const int32_t* cu_host, int32_t S, int32_t T, int32_t* seq_host,
+                      int32_t* pos_host, int32_t* max_seqlen_out);
+
+/*
+ * RoPE prologue, in place ([kime-cpu plan.rs] `Ctx::step` Rope arm;
+ * [kime-cuda plan.rs] `launch_step` Rope arm; [argus text.rs] `rope`).
+ * For every row r < T and every q head (H of them, row r of q at
+ * q + r*q_stride, head h at columns 64h..64h+63) and every k head (G, in k),
+ * with p = pos[r], c = cos[p][i], s = sin[p][i], i < 32:
+ *   x[i]    <- x[i] c - x[i+32] s
+ *   x[i+32] <- x[i+32] c + x[i] s
+ * (half-split pairs, candle's non-interleaved rope).  v is never touched.
+ *   q, k:       device float, rows of at least H*64 / G*64 floats.  For a
+ *               packed qkv row pass k = q + H*64 and the same stride.
+ *   pos:        device int32[T] (from kattn_build_index).
+ *   cos, sin:   device float[table_len][32] (from kattn_rope_tables).
+ * T == 0 queues nothing.  Rows whose pos is outside [0, table_len) are left
+ * unrotated.
+ * Errors: EINVAL (nulls, T < 0, H < 1, G < 0, table_len < 1), EUNSUPPORTED
+ * (head_dim, alignment), EBOUNDS (stride narrower than the row), EDEVICE.
+ */
+int kattn_rope_prologue(float* q, int64_t q_stride, int32_t H, float* k, int64_t k_stride,
+                        int32_t G, const int32_t* pos, int32_t T, const float* cos,
+                        const float* sin, int32_t table_len, int32_t head_dim,
+                        hipStream_t stream);
+
+/* Bytes of device workspace kattn_varlen_fwd needs for this batch shape. */
+size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T);
+
+/*
+ * Varlen attention forward over already-rotated q/k ([kime-cpu plan.rs]
+ * `Ctx::step` Attention arm; [kime-cuda plan.rs] `launch_step` Attention arm;
+ * [argus text.rs] `block`, `CausalSoftmax`).  For every sequence s, row i of
+ * s (position i) and q head h, with g = h / (H/G) (the GQA grouping of
+ * [argus text.rs] `block`: q heads 0..R-1 read kv head 0, and so on):
+ *   out[i][64h..] = sum_j softmax_j(scale * <q_i,h , k_j,g> + M_ij) v_j,g
+ * over keys j of the same sequence, where M_ij = 0 when j is visible and
+ * -inf otherwise.  Visible: (window < 0 or |i - j| <= window / 2) and
+ * (causal == 0 or j <= i).  Masked keys are skipped, which gives the same
+ * result as the -inf mask ([argus text.rs] module docs).
+ *   out:        device float (T, H*64), row stride out_stride.  Rows >= T
+ *               and columns >= H*64 are never written.
+ *   q, k, v:    device float (T, H*64), (T, G*64), (T, G*64) with their own
+ *               strides (a packed qkv row: k = q + H*64, v = k + G*64).
+ *   cu:         device int32[S+1], the offsets of kattn_build_index.
+ *   max_seqlen: longest sequence (host scalar, from kattn_build_index).
+ *   window:     -1 for none (the CUDA page's encoding), else >= 0.
+ *   causal:     0 or 1.
+ *   scale:      finite, > 0; folded into q as it is loaded (exact for 1/8).
+ *   workspace:  device, >= kattn_varlen_fwd_workspace(S, T) bytes, 256-byte
+ *               aligned; holds the query-tile schedule built on the device.
+ * T == 0 or S == 0 queues nothing.
+ * Errors: EINVAL, EUNSUPPORTED (head_dim, H % G, alignment), EBOUNDS
+ * (stride narrower than the row, max_seqlen > T, workspace), EDEVICE.
+ */
+int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                     const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                     const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen, int32_t H,
+                     int32_t G, int32_t head_dim, int32_t window, int32_t causal, float scale,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace kattn_decode needs. */
+size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t max_used);
+
+/*
+ * One decode step against preallocated caches ([argus text.rs] `KvAppend`,
+ * the KV cache part of `block`, and `CausalSoftmax` with offset L-1, where a
+ * decode row sees the whole cache).  For every sequence b with L = used[b]
+ * (counting the new token) and p = L - 1:
+ *   1. the new k (rotated at p when cos != NULL) and the new v are written
+ *      into row p of every kv head of b's caches; no other cache row is
+ *      written;
+ *   2. the new q (rotated at p when cos != NULL, scaled by `scale`) attends,
+ *      head h through kv head h / (H/G), to rows 0..p with no mask:
+ *      out[b][64h..] = sum_j softmax_j(scale * <q_h, k_j>) v_j.
+ *   out:        device float [B][H*64].
+ *   q:          device float [B][H*64] (the new token's q heads).
+ *   k_new, v_new: device float [B][G*64].
+ *   k_cache, v_cache: device float [B][G][cap][64]; row j of kv head g of
+ *               sequence b at ((b*G + g)*cap + j)*64 ([argus text.rs]
+ *               `KvAppend` layout, stacked over the batch).
+ *   used:       device int32[B], 1 <= used[b] <= max_used.
+ *   max_used:   host scalar, 1 <= max_used <= cap; sizes the split over keys.
+ *   cos, sin:   device float[table_len][32] with table_len >= max_used, or
+ *               both NULL when q and k_new are already rotated.
+ *   workspace:  device, >= kattn_decode_workspace(B, H, max_used) bytes,
+ *               256-byte aligned (per-chunk partial max, sum and output).
+ * B == 0 queues nothing.  Sequences whose used[b] is outside [1, max_used]
+ * are skipped (their out row and caches are left untouched).
+ * Errors: EINVAL, EUNSUPPORTED, EBOUNDS (max_used, cap, table_len,
+ * workspace), EDEVICE.
+ */
+int kattn_decode(float* out, const float* q, const float* k_new, const float* v_new,
+                 float* k_cache, float* v_cache, int32_t cap, const int32_t* used,
+                 int32_t max_used, int32_t B, int32_t H, int32_t G, int32_t head_dim,
+                 float scale, const float* cos, const float* sin, int32_t table_len,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATTN_H */

@@ -1,0 +1,186 @@
+"""Host-side checks of libkattn.so that need no GPU.
+
+The library loads and exports every function include/kattn.h declares; the
+host calls (RoPE tables, index build) are checked against the oracle and
+numpy; and every argument check of the device calls fails with its status
+code before anything reaches the device (the pointers passed here are never
+dereferenced).
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+from transformer_attention_varlen_amd import kattn
+
+ROOT = Path(__file__).resolve().parent.parent
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = (ROOT / "include" / "kattn.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 8
+    assert set(names) == set(kattn.EXPORTS)
+    L = kattn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("theta", [10000.0, 100000.0, 160000.0, 500000.0])
+def test_rope_tables_equal_the_oracles_bit_for_bit(theta):
+    c1, s1 = kattn.kattn_rope_tables(theta, 8192)
+    c2, s2 = oracle.rope_tables(theta, 8192)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_rope_tables_reject_bad_arguments():
+    L = kattn.lib()
+    assert L.kattn_rope_tables(0.0, 4, P(256), P(256)) == kattn.KATTN_EINVAL
+    assert b"theta" in L.kattn_last_error()
+    assert L.kattn_rope_tables(float("inf"), 4, P(256), P(256)) == kattn.KATTN_EINVAL
+    assert L.kattn_rope_tables(1e4, -1, P(256), P(256)) == kattn.KATTN_EINVAL
+    assert L.kattn_rope_tables(1e4, 4, None, P(256)) == kattn.KATTN_EINVAL
+    assert L.kattn_rope_tables(1e4, 0, None, None) == kattn.KATTN_OK
+
+
+@pytest.mark.parametrize("lengths", [[37, 91], [0, 5, 0, 1], [1], [], [512] * 3])
+def test_build_index(lengths):
+    lengths = np.array(lengths, np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    seq, pos, mx = kattn.kattn_build_index(cu)
+    s_ref = np.repeat(np.arange(len(lengths)), lengths)
+    p_ref = np.concatenate([np.arange(n) for n in lengths]) if len(lengths) else np.zeros(0)
+    assert np.array_equal(seq, s_ref) and np.array_equal(pos, p_ref)
+    assert mx == (int(lengths.max()) if len(lengths) else 0)
+
+
+@pytest.mark.parametrize("cu", [[1, 4], [0, 3, 2, 5], [0, 4, 6]])
+def test_build_index_rejects_malformed_offsets(cu):
+    cu = np.array(cu, np.int32)
+    L = kattn.lib()
+    S = len(cu) - 1
+    T = 5 if list(cu) == [0, 4, 6] else int(cu[-1])
+    rc = L.kattn_build_index(P(cu.ctypes.data), S, T, None, None, None)
+    assert rc == kattn.KATTN_EBOUNDS
+    assert L.kattn_last_error()
+
+
+def _fwd(**kw):
+    a = dict(out=P(256), out_stride=256, q=P(256), q_stride=768, k=P(256), k_stride=768,
+             v=P(256), v_stride=768, cu=P(256), S=2, T=128, max_seqlen=91, H=4, G=4,
+             head_dim=64, window=-1, causal=0, scale=0.125, workspace=P(4096),
+             workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return kattn.lib().kattn_varlen_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=32), kattn.KATTN_EUNSUPPORTED),
+    (dict(H=4, G=3), kattn.KATTN_EUNSUPPORTED),
+    (dict(H=0), kattn.KATTN_EINVAL),
+    (dict(S=-1), kattn.KATTN_EINVAL),
+    (dict(window=-2), kattn.KATTN_EINVAL),
+    (dict(causal=2), kattn.KATTN_EINVAL),
+    (dict(scale=0.0), kattn.KATTN_EINVAL),
+    (dict(scale=float("nan")), kattn.KATTN_EINVAL),
+    (dict(max_seqlen=129), kattn.KATTN_EBOUNDS),
+    (dict(q=None), kattn.KATTN_EINVAL),
+    (dict(q_stride=200), kattn.KATTN_EBOUNDS),
+    (dict(out_stride=255), kattn.KATTN_EBOUNDS),
+    (dict(k=P(260)), kattn.KATTN_EUNSUPPORTED),
+    (dict(v_stride=770), kattn.KATTN_EUNSUPPORTED),
+    (dict(workspace=P(4096 + 16)), kattn.KATTN_EUNSUPPORTED),
+    (dict(workspace_bytes=16), kattn.KATTN_EBOUNDS),
+])
+def test_varlen_fwd_rejects_bad_arguments_on_the_host(kw, code):
+    assert _fwd(**kw) == code
+    assert kattn.lib().kattn_last_error()
+
+
+def test_varlen_fwd_empty_batch_queues_nothing():
+    assert _fwd(T=0, max_seqlen=0, out=None, q=None) == kattn.KATTN_OK
+    assert _fwd(S=0, T=0, max_seqlen=0) == kattn.KATTN_OK
+    assert kattn.lib().kattn_last_error() == b""
+
+
+def test_varlen_workspace_size_grows_with_the_batch():
+    a = kattn.kattn_varlen_fwd_workspace(2, 128)
+    b = kattn.kattn_varlen_fwd_workspace(64, 16900)
+    assert 0 < a < b
+    # enough for one (sequence, query block) entry per 32 rows plus one per sequence
+    assert b >= 8 * (16900 // 32 + 64)
+
+
+def _rope(**kw):
+    a = dict(q=P(256), q_stride=768, H=4, k=P(256 + 1024), k_stride=768, G=4, pos=P(256), T=128,
+             cos=P(256), sin=P(256), table_len=91, head_dim=64, stream=None)
+    a.update(kw)
+    return kattn.lib().kattn_rope_prologue(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), kattn.KATTN_EUNSUPPORTED),
+    (dict(T=-1), kattn.KATTN_EINVAL),
+    (dict(table_len=0), kattn.KATTN_EINVAL),
+    (dict(pos=None), kattn.KATTN_EINVAL),
+    (dict(q_stride=128), kattn.KATTN_EBOUNDS),
+    (dict(k_stride=100), kattn.KATTN_EBOUNDS),
+    (dict(cos=P(260)), kattn.KATTN_EUNSUPPORTED),
+    (dict(q_stride=770), kattn.KATTN_EUNSUPPORTED),
+])
+def test_rope_prologue_rejects_bad_arguments_on_the_host(kw, code):
+    assert _rope(**kw) == code
+
+
+def test_rope_prologue_empty_batch_queues_nothing():
+    assert _rope(T=0, q=None, k=None) == kattn.KATTN_OK
+
+
+def _dec(**kw):
+    a = dict(out=P(256), q=P(256), k_new=P(256), v_new=P(256), k_cache=P(256), v_cache=P(256),
+             cap=8192, used=P(256), max_used=8000, B=64, H=9, G=3, head_dim=64, scale=0.125,
+             cos=P(256), sin=P(256), table_len=8192, workspace=P(4096), workspace_bytes=1 << 26,
+             stream=None)
+    a.update(kw)
+    return kattn.lib().kattn_decode(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=80), kattn.KATTN_EUNSUPPORTED),
+    (dict(H=9, G=2), kattn.KATTN_EUNSUPPORTED),
+    (dict(H=18, G=1), kattn.KATTN_EUNSUPPORTED),
+    (dict(B=-1), kattn.KATTN_EINVAL),
+    (dict(scale=-1.0), kattn.KATTN_EINVAL),
+    (dict(cap=0), kattn.KATTN_EINVAL),
+    (dict(max_used=0), kattn.KATTN_EBOUNDS),
+    (dict(max_used=8193), kattn.KATTN_EBOUNDS),
+    (dict(cos=None), kattn.KATTN_EINVAL),
+    (dict(table_len=7999), kattn.KATTN_EBOUNDS),
+    (dict(used=None), kattn.KATTN_EINVAL),
+    (dict(k_cache=P(264)), kattn.KATTN_EUNSUPPORTED),
+    (dict(workspace=P(4096 + 64)), kattn.KATTN_EUNSUPPORTED),
+    (dict(workspace_bytes=1024), kattn.KATTN_EBOUNDS),
+])
+def test_decode_rejects_bad_arguments_on_the_host(kw, code):
+    assert _dec(**kw) == code
+
+
+def test_decode_empty_batch_queues_nothing():
+    assert _dec(B=0, out=None) == kattn.KATTN_OK
+
+
+def test_decode_workspace_covers_every_chunk():
+    small = kattn.kattn_decode_workspace(64, 9, 1)
+    big = kattn.kattn_decode_workspace(64, 9, 8192)
+    assert 0 < small < big
+    # per (sequence, chunk, q head): a 64-float partial output plus its max and sum
+    assert big >= 64 * 9 * (8192 // 256) * 66 * 4

@@ -1,0 +1,268 @@
+"""GPU parity: libkattn.so (through its C ABI) against the FP64 CPU oracle.
+
+Tolerances: attention outputs max |gpu - oracle| <= 2e-5 on every element
+compared (FP32 arithmetic in any order against one FP64 rounding, N(0,1)
+inputs); rotated q/k and appended cache rows <= 1e-6 (one or two f32
+roundings of values below 8).  Integer and index work (which rows and cache
+rows are written) is checked exactly.  Full-size workloads run in the launch
+configuration the bench times; where the oracle would take minutes, sampled
+rows are compared (the oracle computes rows one by one).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_attention_varlen_amd import kattn, workloads as wl
+from transformer_attention_varlen_amd.session import DecodeRun, PrefillRun
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-5
+ROPE_ATOL = 1e-6
+D = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kattn.lib()
+
+
+def oracle_prefill(case, rows=None):
+    tables = oracle.rope_tables(case.theta, max(case.max_seqlen, 1))
+    return oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
+                                   case.causal, tables=tables, rows=rows, threads=16)
+
+
+def gpu_prefill(case, pad_rows=0, sentinel=None):
+    run = PrefillRun(case, out_pad_rows=pad_rows)
+    if sentinel is not None:
+        run.out_full.fill_(sentinel)
+    run.step()
+    torch.cuda.synchronize()
+    return run
+
+
+def max_err(a, b):
+    return float(np.max(np.abs(a.astype(np.float64) - b.astype(np.float64)))) if a.size else 0.0
+
+
+# ----------------------------------------------------------------------------- RoPE prologue
+
+@pytest.mark.parametrize("key", ["0", "3a"])
+def test_rope_prologue_matches_oracle(key):
+    case = wl.build(key)
+    run = PrefillRun(case)
+    run.rope()
+    torch.cuda.synchronize()
+    tables = oracle.rope_tables(case.theta, run.table_len)
+    q_ref = oracle.rope_apply(case.q, case.H, run.pos_h, *tables)
+    k_ref = oracle.rope_apply(case.k, case.G, run.pos_h, *tables)
+    assert max_err(run.q.cpu().numpy(), q_ref) <= ROPE_ATOL
+    assert max_err(run.k.cpu().numpy(), k_ref) <= ROPE_ATOL
+    assert np.array_equal(run.v.cpu().numpy(), case.v)   # v is never touched
+
+
+# ----------------------------------------------------------------------------- small prefill cases
+
+RAGGED = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
+SMALL_CASES = [
+    ([37, 91], 4, 4, -1, False),
+    (RAGGED, 4, 4, -1, False),
+    (RAGGED, 4, 4, -1, True),
+    (RAGGED, 4, 4, 0, False),
+    (RAGGED, 4, 4, 1, False),
+    (RAGGED, 4, 4, 5, False),
+    (RAGGED, 4, 4, 128, False),
+    (RAGGED, 4, 4, 300, False),
+    (RAGGED, 4, 4, 40, True),
+    ([130, 7, 300, 1], 9, 3, -1, True),
+    ([130, 7, 300, 1], 9, 3, 64, False),
+    ([130, 7, 300], 6, 2, -1, True),
+    ([130, 7, 300], 8, 2, -1, False),
+    ([130, 7, 300], 5, 1, -1, True),
+    ([130, 7, 300], 2, 2, 33, False),
+    ([0, 45, 0, 0, 17, 0], 4, 2, -1, False),
+    ([0, 45, 0, 0, 17, 0], 4, 2, 6, True),
+]
+
+
+@pytest.mark.parametrize("lengths,H,G,window,causal", SMALL_CASES)
+def test_prefill_small_cases(lengths, H, G, window, causal):
+    case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
+                           theta=10000.0, seed=100 + len(lengths) + H + window)
+    run = gpu_prefill(case, pad_rows=5, sentinel=float("nan"))
+    got = run.out_full.cpu().numpy()
+    ref = oracle_prefill(case)
+    assert max_err(got[:case.T], ref) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))  # rows past T are never written
+
+
+# ----------------------------------------------------------------------------- named workloads
+
+@pytest.mark.parametrize("key", ["0", "1", "3a"])
+def test_workload_full_parity(key):
+    case = wl.build(key)
+    run = gpu_prefill(case)
+    got = run.out.cpu().numpy()
+    ref = oracle_prefill(case)
+    assert max_err(got, ref) <= ATOL
+
+
+def _sample_rows(case, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for s in range(case.S):
+        lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+        if hi > lo:
+            rows.update([lo, lo + 1, hi - 2, hi - 1, (lo + hi) // 2])
+    rows.update(rng.integers(0, case.T, n_random).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < case.T), np.int32)
+
+
+@pytest.mark.parametrize("key", ["2", "3b"])
+def test_workload_sampled_parity(key):
+    case = wl.build(key)
+    run = gpu_prefill(case)
+    got = run.out.cpu().numpy()
+    rows = _sample_rows(case, 24, 7)
+    ref = oracle_prefill(case, rows=rows)
+    assert max_err(got[rows], ref) <= ATOL
+    assert np.all(np.isfinite(got))
+
+
+# ----------------------------------------------------------------------------- GPU invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_of_twice_the_length_is_bit_identical_to_global(causal):
+    lengths = [50, 17, 300, 129]
+    a = wl.make_prefill(lengths, 4, 4, packed=True, window=-1, causal=causal, seed=5)
+    b = wl.make_prefill(lengths, 4, 4, packed=True, window=2 * 300, causal=causal, seed=5)
+    ga = gpu_prefill(a).out.cpu()
+    gb = gpu_prefill(b).out.cpu()
+    assert torch.equal(ga, gb)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (20, False)])
+def test_each_sequence_alone_is_bit_identical_to_its_rows_in_the_batch(window, causal):
+    lengths = [70, 0, 200, 33]
+    case = wl.make_prefill(lengths, 9, 3, packed=False, window=window, causal=causal, seed=6)
+    packed = gpu_prefill(case).out.cpu()
+    for s, n in enumerate(lengths):
+        lo = int(case.cu[s])
+        if n == 0:
+            continue
+        alone = wl.PrefillCase("alone", np.array([n], np.int32), np.array([0, n], np.int32),
+                               9, 3, window, causal, case.theta, case.q[lo:lo + n],
+                               case.k[lo:lo + n], case.v[lo:lo + n])
+        assert torch.equal(gpu_prefill(alone).out.cpu(), packed[lo:lo + n])
+
+
+def test_gqa_matches_mha_with_repeated_kv():
+    H, G = 9, 3
+    case = wl.make_prefill([100, 257], H, G, packed=False, causal=True, seed=8)
+    T = case.T
+    k_rep = np.repeat(case.k.reshape(T, G, 1, D), H // G, axis=2).reshape(T, H * D)
+    v_rep = np.repeat(case.v.reshape(T, G, 1, D), H // G, axis=2).reshape(T, H * D)
+    mha = wl.PrefillCase("mha", case.lengths, case.cu, H, H, -1, True, case.theta, case.q, k_rep,
+                         v_rep)
+    a = gpu_prefill(case).out.cpu().numpy()
+    b = gpu_prefill(mha).out.cpu().numpy()
+    assert max_err(a, b) <= ATOL
+
+
+def test_uniform_weights_recover_the_visible_range_on_gpu():
+    # q = 0: every visible key has weight 1/count; v_j = [1, p_j, p_j^2] recovers the range
+    lengths = [1, 37, 91, 130]
+    for window, causal in [(-1, False), (-1, True), (128, False), (7, True)]:
+        case = wl.make_prefill(lengths, 4, 2, packed=False, window=window, causal=causal, seed=3)
+        case.q[:] = 0.0
+        case.v[:] = 0.0
+        for s in range(case.S):
+            lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+            p = np.arange(hi - lo, dtype=np.float32)
+            for g in range(2):
+                case.v[lo:hi, g * D] = 1.0
+                case.v[lo:hi, g * D + 1] = p
+                case.v[lo:hi, g * D + 2] = p * p
+        got = gpu_prefill(case).out.cpu().numpy()
+        ref = oracle_prefill(case)
+        assert max_err(got[:, 0::D], ref[:, 0::D]) <= 1e-6
+        assert np.allclose(got, ref, rtol=1e-6, atol=1e-4)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _decode_case(lens, H, G, cap, seed):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    return wl.DecodeCase("small", B, H, G, cap, 100000.0,
+                         rng.standard_normal((B, G, cap, D), dtype=np.float32),
+                         rng.standard_normal((B, G, cap, D), dtype=np.float32),
+                         rng.standard_normal((B, H * D), dtype=np.float32),
+                         rng.standard_normal((B, G * D), dtype=np.float32),
+                         rng.standard_normal((B, G * D), dtype=np.float32),
+                         np.array(lens, np.int32))
+
+
+def _check_decode(case, rotate):
+    run = DecodeRun(case, rotate=rotate)
+    run.step()
+    torch.cuda.synchronize()
+    tables = oracle.rope_tables(case.theta, case.cap) if rotate else None
+    ref, kc, vc = oracle.decode(case.q_new, case.k_new, case.v_new, case.k_cache, case.v_cache,
+                                case.used, case.H, case.G, tables=tables, threads=16)
+    assert max_err(run.out.cpu().numpy(), ref) <= ATOL
+    gk = run.k_cache.cpu().numpy()
+    gv = run.v_cache.cpu().numpy()
+    for b, L in enumerate(case.used):
+        p = int(L) - 1
+        assert max_err(gk[b, :, p], kc[b, :, p]) <= ROPE_ATOL
+        assert np.array_equal(gv[b, :, p], vc[b, :, p])
+        gk[b, :, p] = kc[b, :, p]
+    # every other cache row is untouched
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("H,G", [(9, 3), (4, 4), (8, 1)])
+def test_decode_small(rotate, H, G):
+    case = _decode_case([1, 2, 255, 256, 257, 300, 513], H, G, 520, seed=H * 10 + G)
+    _check_decode(case, rotate)
+
+
+def test_decode_full_workload():
+    _check_decode(wl.build("4"), rotate=True)
+
+
+def test_decode_equals_last_causal_row_of_prefill():
+    H, G, L = 9, 3, 700
+    case = wl.make_prefill([L], H, G, packed=False, causal=True, theta=100000.0, seed=12)
+    pre = gpu_prefill(case)
+    last = pre.out.cpu().numpy()[L - 1]
+    cap = 1024
+    kc = np.zeros((1, G, cap, D), np.float32)
+    vc = np.zeros((1, G, cap, D), np.float32)
+    k_rot = pre.k.cpu().numpy()          # rotated by the prologue
+    q_rot = pre.q.cpu().numpy()
+    kc[0, :, :L] = k_rot.reshape(L, G, D).transpose(1, 0, 2)
+    vc[0, :, :L] = case.v.reshape(L, G, D).transpose(1, 0, 2)
+    dec = wl.DecodeCase("dec", 1, H, G, cap, case.theta, kc, vc, q_rot[L - 1:].copy(),
+                        k_rot[L - 1:].copy(), case.v[L - 1:].copy(), np.array([L], np.int32))
+    run = DecodeRun(dec, rotate=False)
+    run.step()
+    torch.cuda.synchronize()
+    assert max_err(run.out.cpu().numpy()[0], last) <= ATOL
+
+
+def test_decode_skips_sequences_with_bad_lengths():
+    case = _decode_case([5, 0, 300], 9, 3, 320, seed=4)
+    run = DecodeRun(case, rotate=True)
+    run.max_used = 300
+    run.out.fill_(7.0)
+    run.step()
+    torch.cuda.synchronize()
+    out = run.out.cpu().numpy()
+    assert np.all(out[1] == 7.0)
+    assert np.array_equal(run.k_cache.cpu().numpy()[1], case.k_cache[1])

@@ -1,0 +1,29 @@
+// internal.h -- host-side helpers shared by the translation units of libkattn.so.
+// Not installed; the public interface is include/kattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kattn.h"
+
+namespace kattn {
+
+constexpr int kHeadDim = 64;
+
+// Records a printf-style message for kattn_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the message (called on every successful entry).
+int ok();
+
+// True when KATTN_CHECK=1 (read once).
+bool debug_checks();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks the launch just queued; returns KATTN_OK or KATTN_EDEVICE.
+int check_launch(const char* what);
+
+}  // namespace kattn

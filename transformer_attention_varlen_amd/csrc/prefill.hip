@@ -1,0 +1,499 @@
+// prefill.hip -- varlen attention forward: FP32-MFMA tile kernel with online softmax.
+//
+// What is computed (kime-cpu plan.rs `Ctx::step` Attention arm, kime-cuda
+// plan.rs `launch_step` Attention arm, argus text.rs `block` and
+// `CausalSoftmax`): for every sequence of the packed batch and every q head,
+// softmax(scale * q k^T + M) v over that sequence's keys, with M = -inf
+// outside the window / causal limit.  q and k arrive already rotated.
+//
+// Design for gfx950 (CDNA4, 64-wide waves, 160 KB LDS per CU):
+//
+// * Work item: a work-group owns QW blocks of 32 query rows of one sequence
+//   and HPW q heads that share one kv head (HPW = q heads per kv head when
+//   that is small), so one K/V tile staged in LDS serves every q head of its
+//   group -- the GQA fold of argus text.rs `block`, without repeat_kv.
+// * One wave = 32 queries x 1 head.  Scores are computed transposed,
+//   S^T = K Q^T, with v_mfma_f32_32x32x2f32: A = 32 keys x 2 dims (LDS), B =
+//   2 dims x 32 queries (registers).  In the 32x32 result lane l holds query
+//   column l%32 and 16 key rows, so the row max over keys is 15 in-lane
+//   maxima plus one exchange with lane l^32, and the running max, sum and the
+//   rescale of O are per lane.
+// * O^T = V^T P^T with the same instruction: the B operand P^T (2 keys x 32
+//   queries) is exactly register r of the score block -- keys 8(r/4)+(r%4)
+//   in lanes 0-31 and that +4 in lanes 32-63 -- so P never leaves registers;
+//   the A operand reads the matching V rows from LDS.
+// * The contraction order over the 64 dims is a free choice: lane half h
+//   feeds dims 32h..32h+31, so each lane's Q slice is 128 contiguous bytes
+//   and K is read as ds_read_b128.  V is read as float2 (dims 2j, 2j+1)
+//   feeding two accumulators, so output dim d = 2i + block.
+// * scale is folded into q as it is loaded: exact for 1/8 (argus text.rs
+//   module docs).  exp is v_exp_f32 on (s - m) * log2(e).
+// * Key tiles outside a query block's window / causal range are never
+//   loaded (never computed, per wave); tiles inside it skip the per-element
+//   mask, and only boundary tiles set masked scores to -inf -- which gives
+//   exactly what the -inf mask gives (argus text.rs module docs).
+// * A one-work-group planning kernel lists the (sequence, first query) tiles
+//   in the workspace, longest key range first, so the heavy tiles start
+//   first and the grid drains evenly.
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "internal.h"
+
+namespace kattn {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BN = 64;        // keys per LDS tile
+constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: exp2 of (-1e30 - m) is 0, never NaN
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 1024;
+
+// Workspace layout (bytes): [0,256) header (tile count), then the tile
+// prefix over sequences (S+1 ints), then the tile list (int2 each).
+constexpr size_t kHeader = 256;
+
+__host__ __device__ inline size_t prefix_bytes(int32_t S) {
+    return ((static_cast<size_t>(S) + 1) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+}
+__host__ __device__ inline int64_t tile_capacity(int32_t S, int32_t T, int BM) {
+    return (static_cast<int64_t>(T) + BM - 1) / BM + S;
+}
+
+struct SeqRange {
+    int lo, n;
+};
+
+__device__ inline SeqRange seq_range(const int32_t* cu, int s, int T) {
+    int lo = cu[s], hi = cu[s + 1];
+    lo = min(max(lo, 0), T);
+    hi = min(max(hi, 0), T);
+    return {lo, max(hi - lo, 0)};
+}
+
+// Key range [kbeg, kend) a block of query rows [q0, qend) may see, kbeg
+// aligned down to BN from the sequence start.  hw < 0: no window.
+__device__ inline void key_range(int q0, int qend, int n, int hw, int causal, int& kbeg,
+                                 int& kend) {
+    const int qlast = qend - 1;
+    int b = 0, e = n;
+    if (hw >= 0) {
+        b = max(0, q0 - hw);
+        e = min(n, qlast + hw + 1);
+    }
+    if (causal) e = min(e, qlast + 1);
+    kbeg = (b / BN) * BN;
+    kend = e;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Planning kernel: one work-group of 1024 threads.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S,
+                                                           int T, int BM, int hw, int causal,
+                                                           int32_t* __restrict__ ws_prefix,
+                                                           int2* __restrict__ tiles,
+                                                           int32_t* __restrict__ count,
+                                                           int64_t capacity) {
+    __shared__ int scan[kPlanThreads];
+    __shared__ int hist[kPlanBins];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        carry = 0;
+        ws_prefix[0] = 0;
+    }
+    // 1. tiles per sequence, inclusive prefix into ws_prefix[1..S]
+    for (int base = 0; base < S; base += kPlanThreads) {
+        const int s = base + tid;
+        int nt = 0;
+        if (s < S) {
+            const SeqRange r = seq_range(cu, s, T);
+            nt = (r.n + BM - 1) / BM;
+        }
+        scan[tid] = nt;
+        __syncthreads();
+        for (int off = 1; off < kPlanThreads; off <<= 1) {
+            const int add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        if (s < S) ws_prefix[s + 1] = carry + scan[tid];
+        __syncthreads();
+        if (tid == kPlanThreads - 1) carry += scan[tid];
+        __syncthreads();
+    }
+    for (int b = tid; b < kPlanBins; b += kPlanThreads) hist[b] = 0;
+    __syncthreads();
+    const int total = static_cast<int>(min(static_cast<int64_t>(carry), capacity));
+    // 2. histogram of key-tile counts; 3. descending bucket offsets; 4. scatter
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int t = tid; t < total; t += kPlanThreads) {
+            int lo = 0, hi = S - 1;  // last s with ws_prefix[s] <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (ws_prefix[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int s = lo;
+            const SeqRange r = seq_range(cu, s, T);
+            const int q0 = (t - ws_prefix[s]) * BM;
+            int kb, ke;
+            key_range(q0, min(q0 + BM, r.n), r.n, hw, causal, kb, ke);
+            const int work = ke > kb ? (ke - kb + BN - 1) / BN : 0;
+            const int bin = min(work, kPlanBins - 1);
+            if (pass == 0) {
+                atomicAdd(&hist[bin], 1);
+            } else {
+                const int at = atomicAdd(&hist[bin], 1);
+                tiles[at] = make_int2(s, q0);
+            }
+        }
+        __syncthreads();
+        if (pass == 0) {
+            // exclusive scan over bins from the heaviest down
+            const int b = kPlanBins - 1 - tid;
+            scan[tid] = (tid < kPlanBins) ? hist[b] : 0;
+            __syncthreads();
+            for (int off = 1; off < kPlanThreads; off <<= 1) {
+                const int add = tid >= off ? scan[tid - off] : 0;
+                __syncthreads();
+                scan[tid] += add;
+                __syncthreads();
+            }
+            const int excl = scan[tid] - hist[b];
+            __syncthreads();
+            hist[b] = excl;
+            __syncthreads();
+        }
+    }
+    if (tid == 0) *count = total;
+}
+
+// ---------------------------------------------------------------------------------------------
+struct FwdParams {
+    float* out;
+    const float* q;
+    const float* k;
+    const float* v;
+    const int32_t* cu;
+    const int2* tiles;
+    const int32_t* count;
+    int64_t out_stride, q_stride, k_stride, v_stride;
+    int T, H, R, nunits, hw, causal;
+    float scale;
+};
+
+template <int HPW, int QW>
+__global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
+    constexpr int NT = 64 * HPW * QW;
+    constexpr int BM = 32 * QW;
+    __shared__ __attribute__((aligned(16))) float Ks[BN * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) float Vs[BN * LDS_STRIDE];
+
+    const int tix = blockIdx.x / p.nunits;
+    const int unit = blockIdx.x - tix * p.nunits;
+    if (tix >= *p.count) return;
+    const int2 tile = p.tiles[tix];
+    const SeqRange sr = seq_range(p.cu, tile.x, p.T);
+    const int lo = sr.lo, n = sr.n, q0 = tile.y;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 31;   // query column of this lane
+    const int hh = lane >> 5;  // lane half
+    const int head = unit * HPW + (wave % HPW);
+    const int g = head / p.R;
+    const int qa = q0 + (wave / HPW) * 32;  // first query of this wave
+    const int qi = qa + j;                  // this lane's query
+    const bool wave_live = qa < n;
+    const int qlast_w = min(qa + 31, n - 1);
+
+    // Q slice: dims 32hh .. 32hh+31 of query qi, times scale.
+    float qreg[32];
+    if (qi < n) {
+        const float4* src = reinterpret_cast<const float4*>(
+            p.q + static_cast<int64_t>(lo + qi) * p.q_stride + head * kHeadDim + hh * 32);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4 t = src[m];
+            qreg[4 * m + 0] = t.x * p.scale;
+            qreg[4 * m + 1] = t.y * p.scale;
+            qreg[4 * m + 2] = t.z * p.scale;
+            qreg[4 * m + 3] = t.w * p.scale;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
+    }
+
+    f32x16 O0, O1;  // O^T accumulators: rows i -> dims 2i (O0) and 2i+1 (O1), column = query j
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        O0[r] = 0.0f;
+        O1[r] = 0.0f;
+    }
+    float m_run = kNegBig;  // running max of this lane's query
+    float l_run = 0.0f;     // running sum over this lane half's keys
+
+    int kbeg, kend;
+    key_range(q0, min(q0 + BM, n), n, p.hw, p.causal, kbeg, kend);
+
+    const float* kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
+    const float* vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
+
+    for (int kt = kbeg; kt < kend; kt += BN) {
+        __syncthreads();  // the previous tile has been read by every wave
+        for (int idx = threadIdx.x; idx < BN * 16; idx += NT) {
+            const int r = idx >> 4, c = idx & 15;
+            const int key = kt + r;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (key < n) {
+                kv = reinterpret_cast<const float4*>(kbase + static_cast<int64_t>(key) * p.k_stride)[c];
+                vv = reinterpret_cast<const float4*>(vbase + static_cast<int64_t>(key) * p.v_stride)[c];
+            }
+            *reinterpret_cast<float4*>(&Ks[r * LDS_STRIDE + 4 * c]) = kv;
+            *reinterpret_cast<float4*>(&Vs[r * LDS_STRIDE + 4 * c]) = vv;
+        }
+        __syncthreads();
+
+        // Does this wave see any key of the tile, and all of them?
+        const int klast = kt + BN - 1;
+        bool any = wave_live && kt < n;
+        bool full = wave_live && klast < n;
+        if (p.causal) {
+            any = any && kt <= qlast_w;
+            full = full && klast <= qa;
+        }
+        if (p.hw >= 0) {
+            any = any && kt <= qlast_w + p.hw && klast >= qa - p.hw;
+            full = full && kt >= qlast_w - p.hw && klast <= qa + p.hw;
+        }
+        if (!any) continue;
+
+        // S^T = K Q^T for keys kt..kt+31 (S0) and kt+32..kt+63 (S1).
+        f32x16 S0, S1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            S0[r] = 0.0f;
+            S1[r] = 0.0f;
+        }
+        const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
+        const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
+            const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
+        }
+
+        if (!full) {
+            // boundary tile: masked scores become -inf (the same as skipping them)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int key1 = key0 + 32;
+                bool v0 = key0 < n, v1 = key1 < n;
+                if (p.causal) {
+                    v0 = v0 && key0 <= qi;
+                    v1 = v1 && key1 <= qi;
+                }
+                if (p.hw >= 0) {
+                    v0 = v0 && abs(qi - key0) <= p.hw;
+                    v1 = v1 && abs(qi - key1) <= p.hw;
+                }
+                if (!v0) S0[r] = -INFINITY;
+                if (!v1) S1[r] = -INFINITY;
+            }
+        }
+
+        // online softmax
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+        const float ml = m_new * kLog2e;
+        m_run = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
+            S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
+            psum += S0[r] + S1[r];
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            O0[r] *= alpha;
+            O1[r] *= alpha;
+        }
+
+        // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
+            const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
+            const float2 vb =
+                *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
+            O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
+            O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
+            O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
+            O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qi < n) {
+        const float inv = 1.0f / l_tot;
+        float* dst = p.out + static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim;
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            const int i0 = 8 * grp + 4 * hh;  // result rows i0..i0+3 -> dims 2*i0 .. 2*i0+7
+            const int r0 = 4 * grp;
+            float4 a, b;
+            a.x = O0[r0 + 0] * inv;
+            a.y = O1[r0 + 0] * inv;
+            a.z = O0[r0 + 1] * inv;
+            a.w = O1[r0 + 1] * inv;
+            b.x = O0[r0 + 2] * inv;
+            b.y = O1[r0 + 2] * inv;
+            b.z = O0[r0 + 3] * inv;
+            b.w = O1[r0 + 3] * inv;
+            *reinterpret_cast<float4*>(dst + 2 * i0) = a;
+            *reinterpret_cast<float4*>(dst + 2 * i0 + 4) = b;
+        }
+    }
+}
+
+// Work-group shape per q-heads-per-kv-head ratio R: HPW heads x QW query blocks.
+struct Shape {
+    int hpw, qw;
+};
+Shape pick_shape(int R) {
+    switch (R) {
+        case 1: return {1, 4};
+        case 2: return {2, 2};
+        case 3: return {3, 2};
+        case 4: return {4, 1};
+        default: return {1, 4};
+    }
+}
+
+template <int HPW, int QW>
+void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_kernel<HPW, QW>), dim3(static_cast<unsigned>(grid)), dim3(64 * HPW * QW),
+                       0, stream, p);
+}
+
+}  // namespace
+}  // namespace kattn
+
+using namespace kattn;
+
+extern "C" size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T) {
+    if (S < 0 || T < 0) return 0;
+    // the smallest query block (32 rows) bounds the tile count of every shape
+    return kHeader + prefix_bytes(S) + static_cast<size_t>(tile_capacity(S, T, 32)) * sizeof(int2);
+}
+
+extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                                const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                                const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen,
+                                int32_t H, int32_t G, int32_t head_dim, int32_t window,
+                                int32_t causal, float scale, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kattn_varlen_fwd";
+    if (head_dim != kHeadDim)
+        return fail(KATTN_EUNSUPPORTED, "%s: head_dim %d, only 64 is supported", fn, head_dim);
+    if (S < 0 || T < 0 || H < 1 || G < 1)
+        return fail(KATTN_EINVAL, "%s: S=%d T=%d H=%d G=%d", fn, S, T, H, G);
+    if (H % G != 0) return fail(KATTN_EUNSUPPORTED, "%s: H=%d is not a multiple of G=%d", fn, H, G);
+    if (window < -1) return fail(KATTN_EINVAL, "%s: window %d (use -1 for none)", fn, window);
+    if (causal != 0 && causal != 1) return fail(KATTN_EINVAL, "%s: causal must be 0 or 1", fn);
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(KATTN_EINVAL, "%s: scale must be finite and > 0", fn);
+    if (max_seqlen < 0 || max_seqlen > T)
+        return fail(KATTN_EBOUNDS, "%s: max_seqlen %d outside [0, T=%d]", fn, max_seqlen, T);
+    if (T == 0 || S == 0) return ok();
+    if (!out || !q || !k || !v || !cu || !workspace) return fail(KATTN_EINVAL, "%s: null pointer", fn);
+    if (out_stride < static_cast<int64_t>(H) * kHeadDim || q_stride < static_cast<int64_t>(H) * kHeadDim ||
+        k_stride < static_cast<int64_t>(G) * kHeadDim || v_stride < static_cast<int64_t>(G) * kHeadDim)
+        return fail(KATTN_EBOUNDS, "%s: a row stride is narrower than its heads", fn);
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || (out_stride & 3) ||
+        (q_stride & 3) || (k_stride & 3) || (v_stride & 3))
+        return fail(KATTN_EUNSUPPORTED, "%s: pointers and strides must be multiples of 16 bytes", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+    const size_t need = kattn_varlen_fwd_workspace(S, T);
+    if (workspace_bytes < need)
+        return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+    if (debug_checks()) {
+        std::vector<int32_t> h(static_cast<size_t>(S) + 1);
+        if (hipMemcpy(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(KATTN_EDEVICE, "%s: KATTN_CHECK copy of cu failed", fn);
+        if (h[0] != 0 || h[S] != T) return fail(KATTN_EBOUNDS, "%s: cu[0]=%d cu[S]=%d T=%d", fn, h[0], h[S], T);
+        for (int32_t s = 0; s < S; ++s) {
+            if (h[s + 1] < h[s]) return fail(KATTN_EBOUNDS, "%s: cu decreases at %d", fn, s);
+            if (h[s + 1] - h[s] > max_seqlen)
+                return fail(KATTN_EBOUNDS, "%s: sequence %d longer than max_seqlen", fn, s);
+        }
+    }
+
+    const int R = H / G;
+    const Shape sh = pick_shape(R);
+    const int BM = 32 * sh.qw;
+    const int64_t capacity = tile_capacity(S, T, BM);
+    const int nunits = H / sh.hpw;
+    const int64_t grid = capacity * nunits;
+    if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
+    // half window; a window wider than the batch is the same as none of that width
+    const int hw = window < 0 ? -1 : std::min(window / 2, T);
+
+    char* ws = static_cast<char*>(workspace);
+    int32_t* count = reinterpret_cast<int32_t*>(ws);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
+    int2* tiles = reinterpret_cast<int2*>(ws + kHeader + prefix_bytes(S));
+
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw, causal,
+                       prefix, tiles, count, capacity);
+    int rc = check_launch(fn);
+    if (rc != KATTN_OK) return rc;
+
+    FwdParams p;
+    p.out = out;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.cu = cu;
+    p.tiles = tiles;
+    p.count = count;
+    p.out_stride = out_stride;
+    p.q_stride = q_stride;
+    p.k_stride = k_stride;
+    p.v_stride = v_stride;
+    p.T = T;
+    p.H = H;
+    p.R = R;
+    p.nunits = nunits;
+    p.hw = hw;
+    p.causal = causal;
+    p.scale = scale;
+    if (sh.hpw == 1) launch_fwd<1, 4>(p, grid, stream);
+    else if (sh.hpw == 2) launch_fwd<2, 2>(p, grid, stream);
+    else if (sh.hpw == 3) launch_fwd<3, 2>(p, grid, stream);
+    else launch_fwd<4, 1>(p, grid, stream);
+    return check_launch(fn);
+}
