@@ -48,17 +48,25 @@ def parse():
                     help="budget for the CPU oracle baseline (0 disables)")
     ap.add_argument("--only", default=None,
                     help="run only this workload's loop (for profiling): 1, 2, 3a, 3b or 4")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="with --only: also run one plain device copy of this many MiB, the "
+                         "known-size kernel that scales PMC byte counters")
     return ap.parse_args()
 
 
 class Flusher:
-    """Writes a buffer larger than L2 + MALL so the next call starts cold."""
+    """Reads a buffer larger than L2 + MALL so the next call starts cold.
+
+    A read pass leaves clean lines behind; a write pass would leave dirty lines
+    that the timed call then pays to write back."""
 
     def __init__(self, torch, nbytes=1 << 30):
-        self.buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def __call__(self):
-        self.buf.fill_(1.0)
+        torch_sum = self.buf.sum
+        self.sink.copy_(torch_sum())
 
 
 def time_calls(torch, fn, steps, warmup, flush=None):
@@ -123,15 +131,16 @@ def decode_part(torch, steps, warmup, flush):
 
 
 def cpu_baseline(case, budget_s):
-    """The oracle, untuned, on a random sample of the workload's rows (all heads each)."""
+    """The oracle, untuned, on random samples of the workload's rows (all heads each),
+    repeated until the time budget is spent."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
     tables = oracle.rope_tables(case.theta, max(int(case.lengths.max()), 1))
     rng = np.random.default_rng(0)
-    n = 64
+    n = 256
     spent = 0.0
     done = 0
-    while True:
+    while spent < budget_s:
         rows = np.sort(rng.integers(0, case.T, n)).astype(np.int32)
         t0 = time.perf_counter()
         oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
@@ -139,13 +148,13 @@ def cpu_baseline(case, budget_s):
         dt = time.perf_counter() - t0
         spent += dt
         done += n
-        if spent >= budget_s or done >= case.T:
-            break
-        n = int(min(max(n * 2, 1), max(1, (budget_s - spent) / max(dt / n, 1e-9))))
+        per_row = dt / n
+        n = int(min(max(1, (budget_s - spent) / max(per_row, 1e-9)), 4 * n, case.T))
     return {"value": round(done / spent / 1e6, 6), "unit": "Mtok/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} random query rows (all {case.H} heads, RoPE + -inf mask + two-pass "
-                      f"softmax in FP64) of the headline workload, {spent:.1f} s"}
+            "sample": f"{done} query rows drawn uniformly (with replacement) from the headline "
+                      f"workload, all {case.H} heads each (RoPE, -inf mask, two-pass softmax in "
+                      f"FP64), {spent:.1f} s"}
 
 
 def main():
@@ -176,7 +185,15 @@ def main():
         for _ in range(args.warmup + args.steps):
             fn()
         torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup}))
+        if args.calib_copy_mib > 0:
+            n = args.calib_copy_mib * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup,
+                          "calib_copy_mib": args.calib_copy_mib}))
         return
 
     case = wl.build(HEADLINE)

@@ -8,20 +8,21 @@
 // its q heads (the GQA fold of argus `block`, without repeat_kv).
 //
 // Design for gfx950: the step is HBM bound (each cached row is 256 bytes of
-// K and 256 of V, used once per q head of the group, in registers).
+// K and 256 of V, read once and used for every q head of its group).
 //
 // * Split over keys: a work-item is (sequence b, kv head g, chunk c of
-//   kChunk rows).  One wave streams its chunk; its four 16-lane groups take
-//   consecutive rows, so each 16-byte load instruction reads 1 KB of
-//   contiguous cache (4 rows) and every byte of HBM is read once.
-// * A lane holds 4 dims of a row; the dot product over a row is a 16-lane sum
-//   done with DPP row permutes (no LDS).  Each group keeps its own running
-//   max, sum and 4 output dims per q head; the four groups are merged once at
-//   the end of the chunk, and the chunk's (max, sum, o[64]) per q head goes
-//   to the workspace.
-// * The append is fused: the work-item whose chunk holds row p writes the
-//   rotated new key and the new value to the cache and uses those values from
-//   registers for row p (no read-after-write through memory).
+//   kChunk rows), one wave each.  Rows are read 4 per 16-byte load
+//   instruction (16 lanes per 256-byte row), so each instruction reads 1 KB
+//   of contiguous cache.
+// * Per block of 32 rows the K rows go through LDS (XOR-swizzled 16-byte
+//   chunks, conflict-free both ways) so that each lane then scores one row:
+//   the softmax math (max, exp, sum) runs once per row instead of once per
+//   lane of a row.  The half-waves take 32 dims each and add their halves.
+//   The probabilities go back through LDS as broadcasts for the P.V update,
+//   which keeps V in the coalesced 4-dims-per-lane layout (no LDS for V).
+// * The append is fused: the work-item whose chunk holds row p = L-1 writes
+//   the rotated new key and the new value to the cache and substitutes them
+//   in registers for that row (no read-after-write through memory).
 // * A combine kernel merges the chunks of each (b, h) with the exact
 //   log-sum-exp algebra and writes the output row.
 
@@ -35,20 +36,11 @@ namespace kattn {
 namespace {
 
 constexpr int kChunk = 256;       // keys per split-K work-item
-constexpr int kRowsPerIter = 16;  // rows a wave loads per iteration: 4 per group
+constexpr int kBlock = 32;        // keys scored together: one per lane of a half-wave
+constexpr int kWaves = 4;         // independent work-items per work-group (one per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kMaxR = 8;          // q heads per kv head handled in registers
-
-__device__ inline float dpp_sum16(float x) {
-    // butterfly over the 16 lanes of a DPP row: lanes ^1, ^2 (quad permutes), then the
-    // 8-lane and 16-lane mirrors, after which every lane holds the row's total
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-    return x;
-}
 
 // Rotated value of dims 4t..4t+3 of one 64-wide head at table row p (half-split pairs).
 __device__ inline float4 rope4(const float* __restrict__ x, int t, const float* __restrict__ cos_t,
@@ -86,38 +78,96 @@ struct DecParams {
     const float* sin_t;
     float* part_o;   // [B][nch][H][64]
     float* part_ml;  // [B][nch][H][2]
-    int cap, max_used, nch, H, G, R;
+    int cap, max_used, nch, chunk, B, H, G, R;
     float scale;
 };
 
+// Orders LDS accesses between the lanes of one wave (waves of a work-group never share LDS).
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Cross-lane reductions on the VALU (DPP row permutes and the gfx950 permlane swaps), so a
+// reduction is a few dependent ALU ops instead of a chain of LDS permutes.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// max / sum over each 16-lane row (quad ^1, quad ^2, half-row mirror, row mirror)
+__device__ inline float row_max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+__device__ inline float row_sum16(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+// rows 0+1 and rows 2+3 combined (v_permlane16_swap): lanes 0-31 and 32-63 each see their half
+__device__ inline float pair_rows_max(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float pair_rows_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// x(lane) + x(lane ^ 32) (v_permlane32_swap)
+__device__ inline float halves_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 template <int R>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) {
+    // Per wave: K rows of the current block, 16-byte chunks XOR-swizzled by row so that both
+    // the row-major staging writes and the one-row-per-lane reads are bank-conflict free;
+    // the rotated, scaled q heads; the block's probabilities.
+    __shared__ __attribute__((aligned(16))) float Ks_all[kWaves][kBlock * 64];
+    __shared__ __attribute__((aligned(16))) float Qs_all[kWaves][R * 64];
+    __shared__ __attribute__((aligned(16))) float Ps_all[kWaves][R * kBlock];
+    const int wave = threadIdx.x >> 6;
+    float* Ks = Ks_all[wave];
+    float* Qs = Qs_all[wave];
+    float* Ps = Ps_all[wave];
+
+    // Work-items run chunk-major -- every (kv head, sequence) of chunk 0, then chunk 1, ... --
+    // so the items past a short sequence's end sit at the back of the grid.
+    const int item = blockIdx.x * kWaves + wave;
+    const int g = item % p.G;
+    const int b = (item / p.G) % p.B;
+    const int c = item / (p.G * p.B);
+    if (c >= p.nch) return;
     const int L = p.used[b];
     if (L < 1 || L > p.max_used) return;
-    const int c0 = c * kChunk;
+    const int c0 = c * p.chunk;
     if (c0 >= L) return;
-    const int c1 = min(c0 + kChunk, L);
     const int pnew = L - 1;
-    const int lane = threadIdx.x;
-    const int t = lane & 15;   // dims 4t..4t+3
-    const int grp = lane >> 4; // row stream of this lane
+    const int c1 = min(c0 + p.chunk, L);  // rows [c0, c1); row pnew comes from k_new / v_new
+    const bool owns_new = pnew < c1;
+    const int lane = threadIdx.x & 63;
+    const int t = lane & 15;    // staging / P.V layout: dims 4t..4t+3 ...
+    const int grp = lane >> 4;  // ... of rows 4i + grp of the block
+    const int j = lane & 31;    // scoring layout: row j of the block ...
+    const int hf = lane >> 5;   // ... dims 32hf .. 32hf+31
 
-    // the new query heads of this group, rotated at pnew and scaled
-    float4 qv[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int h = g * R + u;
-        float4 x = rope4(p.q + (static_cast<int64_t>(b) * p.H + h) * 64, t, p.cos_t, p.sin_t, pnew);
-        qv[u] = make_float4(x.x * p.scale, x.y * p.scale, x.z * p.scale, x.w * p.scale);
+    for (int u = grp; u < R; u += 4) {
+        const float4 x =
+            rope4(p.q + (static_cast<int64_t>(b) * p.H + g * R + u) * 64, t, p.cos_t, p.sin_t, pnew);
+        *reinterpret_cast<float4*>(&Qs[u * 64 + 4 * t]) =
+            make_float4(x.x * p.scale, x.y * p.scale, x.z * p.scale, x.w * p.scale);
     }
 
     const int64_t head_off = (static_cast<int64_t>(b) * p.G + g) * p.cap;
-    const float* kb = p.k_cache + head_off * 64;
-    const float* vb = p.v_cache + head_off * 64;
+    const float4* kb = reinterpret_cast<const float4*>(p.k_cache + head_off * 64) + t;
+    const float4* vb = reinterpret_cast<const float4*>(p.v_cache + head_off * 64) + t;
 
-    // the append: the chunk that holds row pnew owns it
-    const bool owns_new = pnew >= c0 && pnew < c1;
+    // the appended row: rotated new key and new value, written to cache row pnew
     float4 knew = make_float4(0.f, 0.f, 0.f, 0.f), vnew = knew;
     if (owns_new) {
         const int64_t kv_off = (static_cast<int64_t>(b) * p.G + g) * 64;
@@ -129,121 +179,179 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         }
     }
 
-    float m_run[R], l_run[R];
+    float m[R], lp[R];
     float4 o[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        m_run[u] = kNegBig;
-        l_run[u] = 0.0f;
+        m[u] = kNegBig;
+        lp[u] = 0.0f;
         o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    for (int base = c0; base < c1; base += kRowsPerIter) {
-        float4 kr[4], vr[4];
-        int row[4];
+    for (int base = c0; base < c1; base += kBlock) {
+        // 1. K and V rows base + 4i + grp (clamped: always in bounds; extra rows are masked)
+        float4 kr[kBlock / 4], vr[kBlock / 4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            row[i] = base + 4 * i + grp;
-            if (row[i] < c1) {
-                kr[i] = reinterpret_cast<const float4*>(kb + static_cast<int64_t>(row[i]) * 64)[t];
-                vr[i] = reinterpret_cast<const float4*>(vb + static_cast<int64_t>(row[i]) * 64)[t];
-            } else {
-                kr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                vr[i] = kr[i];
-            }
-            if (owns_new && row[i] == pnew) {
-                kr[i] = knew;
-                vr[i] = vnew;
+        for (int i = 0; i < kBlock / 4; ++i) {
+            const int r = min(base + 4 * i + grp, c1 - 1);
+            kr[i] = kb[static_cast<int64_t>(r) * 16];
+            vr[i] = vb[static_cast<int64_t>(r) * 16];
+        }
+        if (owns_new && base + kBlock > pnew) {  // the block holding the new row
+#pragma unroll
+            for (int i = 0; i < kBlock / 4; ++i) {
+                if (base + 4 * i + grp == pnew) {
+                    kr[i] = knew;
+                    vr[i] = vnew;
+                }
             }
         }
+        wave_sync();  // the previous block's reads of Ks / Ps are done
+#pragma unroll
+        for (int i = 0; i < kBlock / 4; ++i) {
+            const int row = 4 * i + grp;
+            *reinterpret_cast<float4*>(&Ks[row * 64 + 4 * (t ^ (row & 15))]) = kr[i];
+        }
+        wave_sync();
+
+        // 2. scores: lane (hf, j) dots row j over dims 32hf..32hf+31, halves then summed.
+        // q is read from LDS each block: an opaque offset keeps the compiler from hoisting
+        // the 32R loop-invariant reads into registers (which would cost occupancy).
+        int qoff = 0;
+        asm volatile("" : "+s"(qoff));
+        qoff &= ~3;  // keeps the 16-byte alignment visible, so q is read as ds_read_b128
+        float s[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) s[u] = 0.0f;
+#pragma unroll 2
+        for (int cc = 0; cc < 8; ++cc) {
+            const int chunk = 8 * hf + cc;
+            const float4 kk = *reinterpret_cast<const float4*>(&Ks[j * 64 + 4 * (chunk ^ (j & 15))]);
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float4 qq = *reinterpret_cast<const float4*>(&Qs[qoff + u * 64 + 4 * chunk]);
+                s[u] = __builtin_fmaf(kk.x, qq.x, s[u]);
+                s[u] = __builtin_fmaf(kk.y, qq.y, s[u]);
+                s[u] = __builtin_fmaf(kk.z, qq.z, s[u]);
+                s[u] = __builtin_fmaf(kk.w, qq.w, s[u]);
+            }
+        }
+        const bool valid = base + j < c1;
+
+        // 3. online softmax over the block's 32 rows (both halves hold the same values)
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            float s[4];
+            const float sv = valid ? halves_sum(s[u]) : -INFINITY;
+            const float mx = pair_rows_max(row_max16(sv));
+            const float m_new = fmaxf(m[u], mx);
+            const float alpha = __builtin_amdgcn_exp2f((m[u] - m_new) * kLog2e);
+            const float pu = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kLog2e, -m_new * kLog2e));
+            m[u] = m_new;
+            lp[u] = __builtin_fmaf(lp[u], alpha, pu);
+            o[u] = make_float4(o[u].x * alpha, o[u].y * alpha, o[u].z * alpha, o[u].w * alpha);
+            // row j = 4i + grp' goes to slot grp'*8 + i, so a P.V lane reads 8 in a row
+            if (hf == 0) Ps[u * kBlock + (j & 3) * (kBlock / 4) + (j >> 2)] = pu;
+        }
+        wave_sync();
+
+        // 4. O += P V over the block
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float d = qv[u].x * kr[i].x;
-                d = __builtin_fmaf(qv[u].y, kr[i].y, d);
-                d = __builtin_fmaf(qv[u].z, kr[i].z, d);
-                d = __builtin_fmaf(qv[u].w, kr[i].w, d);
-                d = dpp_sum16(d);
-                s[i] = row[i] < c1 ? d : -INFINITY;
-            }
-            const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            const float m_new = fmaxf(m_run[u], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * kLog2e);
-            const float ml = m_new * kLog2e;
-            m_run[u] = m_new;
-            float pr[4];
+        for (int u = 0; u < R; ++u) {
+            const float4 pa = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8]);
+            const float4 pb = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8 + 4]);
+            const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            float4 acc = o[u];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], kLog2e, -ml));
-            l_run[u] = l_run[u] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            float4 acc = make_float4(o[u].x * alpha, o[u].y * alpha, o[u].z * alpha, o[u].w * alpha);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc.x = __builtin_fmaf(pr[i], vr[i].x, acc.x);
-                acc.y = __builtin_fmaf(pr[i], vr[i].y, acc.y);
-                acc.z = __builtin_fmaf(pr[i], vr[i].z, acc.z);
-                acc.w = __builtin_fmaf(pr[i], vr[i].w, acc.w);
+            for (int i = 0; i < kBlock / 4; ++i) {
+                acc.x = __builtin_fmaf(pw[i], vr[i].x, acc.x);
+                acc.y = __builtin_fmaf(pw[i], vr[i].y, acc.y);
+                acc.z = __builtin_fmaf(pw[i], vr[i].z, acc.z);
+                acc.w = __builtin_fmaf(pw[i], vr[i].w, acc.w);
             }
             o[u] = acc;
         }
     }
 
-    // merge the four row streams (lanes t, t+16, t+32, t+48) and store the chunk's partials
+    // the chunk's partials: max (uniform), sum over the 32 rows, output summed over the 4 groups
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        float M = fmaxf(m_run[u], __shfl_xor(m_run[u], 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = __builtin_amdgcn_exp2f((m_run[u] - M) * kLog2e);
-        float l = l_run[u] * f;
-        float4 acc = make_float4(o[u].x * f, o[u].y * f, o[u].z * f, o[u].w * f);
-#pragma unroll
-        for (int msk = 16; msk <= 32; msk <<= 1) {
-            l += __shfl_xor(l, msk);
-            acc.x += __shfl_xor(acc.x, msk);
-            acc.y += __shfl_xor(acc.y, msk);
-            acc.z += __shfl_xor(acc.z, msk);
-            acc.w += __shfl_xor(acc.w, msk);
-        }
-        const int h = g * R + u;
-        const int64_t slot = (static_cast<int64_t>(b) * p.nch + c) * p.H + h;
+        // lanes 0-31 hold one copy of each row's sum (lanes 32-63 repeat them)
+        const float l = halves_sum(pair_rows_sum(row_sum16(hf == 0 ? lp[u] : 0.0f)));
+        float4 acc = o[u];
+        acc.x = halves_sum(pair_rows_sum(acc.x));
+        acc.y = halves_sum(pair_rows_sum(acc.y));
+        acc.z = halves_sum(pair_rows_sum(acc.z));
+        acc.w = halves_sum(pair_rows_sum(acc.w));
+        const int64_t slot = (static_cast<int64_t>(b) * p.nch + c) * p.H + g * R + u;
         if (grp == 0) reinterpret_cast<float4*>(p.part_o + slot * 64)[t] = acc;
         if (lane == 0) {
-            p.part_ml[slot * 2 + 0] = M;
+            p.part_ml[slot * 2 + 0] = m[u];
             p.part_ml[slot * 2 + 1] = l;
         }
     }
 }
 
-// One work-group per sequence, one wave per q head: merge the chunks.
-__global__ __launch_bounds__(256) void decode_combine_kernel(float* __restrict__ out,
-                                                             const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             const int32_t* __restrict__ used,
-                                                             int max_used, int nch, int H) {
-    const int b = blockIdx.x;
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// One wave per (q head, sequence): lanes take chunks for the max and the sum, then
+// output dims for the weighted sum of the chunks' partial outputs (8 loads in flight).
+__global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ out,
+                                                            const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            const int32_t* __restrict__ used,
+                                                            int max_used, int nch, int H,
+                                                            int chunk) {
+    const int h = blockIdx.x, b = blockIdx.y;
     const int L = used[b];
     if (L < 1 || L > max_used) return;
-    const int nc = (L + kChunk - 1) / kChunk;
-    const int d = threadIdx.x & 63;
-    for (int h = threadIdx.x >> 6; h < H; h += blockDim.x >> 6) {
-        float M = kNegBig;
-        for (int c = 0; c < nc; ++c)
-            M = fmaxf(M, part_ml[((static_cast<int64_t>(b) * nch + c) * H + h) * 2]);
-        float l = 0.0f, acc = 0.0f;
-        for (int c = 0; c < nc; ++c) {
-            const int64_t slot = (static_cast<int64_t>(b) * nch + c) * H + h;
-            const float f = __builtin_amdgcn_exp2f((part_ml[slot * 2] - M) * kLog2e);
-            l = __builtin_fmaf(part_ml[slot * 2 + 1], f, l);
-            acc = __builtin_fmaf(part_o[slot * 64 + d], f, acc);
+    const int nc = (L + chunk - 1) / chunk;
+    const int lane = threadIdx.x;
+    const int64_t base = static_cast<int64_t>(b) * nch * H + h;  // slot of chunk c: base + c*H
+    float mloc = kNegBig;
+    for (int c = lane; c < nc; c += 64) mloc = fmaxf(mloc, part_ml[(base + static_cast<int64_t>(c) * H) * 2]);
+    const float M = wave_max(mloc);
+    float lsum = 0.0f, acc = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        float f = 0.0f;
+        if (c < nc) {
+            const int64_t slot = base + static_cast<int64_t>(c) * H;
+            f = __builtin_amdgcn_exp2f((part_ml[slot * 2] - M) * kLog2e);
+            lsum = __builtin_fmaf(part_ml[slot * 2 + 1], f, lsum);
         }
-        out[(static_cast<int64_t>(b) * H + h) * 64 + d] = acc / l;
+        const int n = min(64, nc - c0);
+        for (int i0 = 0; i0 < n; i0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int ci = c0 + min(i0 + k, n - 1);
+                v[k] = part_o[(base + static_cast<int64_t>(ci) * H) * 64 + lane];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float fk = __shfl(f, min(i0 + k, 63));
+                acc = i0 + k < n ? __builtin_fmaf(v[k], fk, acc) : acc;
+            }
+        }
     }
+    const float l = wave_sum(lsum);
+    out[(static_cast<int64_t>(b) * H + h) * 64 + lane] = acc / l;
 }
 
 template <int R>
 void launch_split(const DecParams& p, int B, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<R>), dim3(p.nch, p.G, B), dim3(64), 0, stream, p);
+    const int64_t items = static_cast<int64_t>(p.nch) * B * p.G;
+    hipLaunchKernelGGL((decode_split_kernel<R>), dim3(static_cast<unsigned>((items + kWaves - 1) / kWaves)),
+                       dim3(64 * kWaves), 0, stream, p);
 }
 
 size_t part_bytes(int32_t B, int32_t H, int32_t nch) {
@@ -304,8 +412,8 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
                 return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [1, max_used=%d]", fn, i, h[i], max_used);
     }
     const int32_t nch = (max_used + kChunk - 1) / kChunk;
-    if (static_cast<int64_t>(B) > 65535 || G > 65535)
-        return fail(KATTN_EBOUNDS, "%s: B or G above the grid limit", fn);
+    if (B > 65535 || static_cast<int64_t>(nch) * B * G / kWaves >= 0x7fffffff)
+        return fail(KATTN_EBOUNDS, "%s: batch above the grid limit", fn);
 
     DecParams p;
     p.q = q;
@@ -323,6 +431,8 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     p.cap = cap;
     p.max_used = max_used;
     p.nch = nch;
+    p.chunk = kChunk;
+    p.B = B;
     p.H = H;
     p.G = G;
     p.R = H / G;
@@ -339,7 +449,7 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     }
     int rc = check_launch(fn);
     if (rc != KATTN_OK) return rc;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(B), dim3(256), 0, stream, out, p.part_o, p.part_ml,
-                       used, max_used, nch, H);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(H, B), dim3(64), 0, stream, out, p.part_o,
+                       p.part_ml, used, max_used, nch, H, p.chunk);
     return check_launch(fn);
 }

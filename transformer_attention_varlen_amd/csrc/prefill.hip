@@ -386,7 +386,7 @@ Shape pick_shape(int R) {
     switch (R) {
         case 1: return {1, 4};
         case 2: return {2, 2};
-        case 3: return {3, 2};
+        case 3: return {1, 4};
         case 4: return {4, 1};
         default: return {1, 4};
     }
