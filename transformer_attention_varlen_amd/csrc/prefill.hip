@@ -188,7 +188,10 @@ struct FwdParams {
     float scale;
 };
 
-template <int HPW, int QW>
+// BAND: the launch has a window or a causal limit, so a wave may skip half tiles that fall
+// outside its band; without one (global attention) every half tile a wave reaches is live
+// except at a sequence's ragged end, and the single-half path is left out of the code.
+template <int HPW, int QW, bool BAND>
 __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
     constexpr int NT = 64 * HPW * QW;
     constexpr int BM = 32 * QW;
@@ -246,114 +249,205 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
     const float* kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
     const float* vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
 
+    // K/V tiles are staged through LDS.  The next tile's rows are loaded into registers
+    // before this tile's MFMA work and written to LDS after it, so the global-load latency
+    // overlaps the compute.  Rows past the sequence are clamped to its last row (in bounds,
+    // finite) and always masked: a tile holding them never takes the unmasked path.
+    static_assert(BN * 16 == 4 * NT, "each thread stages 4 pieces of K and 4 of V per tile");
+    const int lrow = threadIdx.x >> 4;  // rows lrow + 16i of the tile, piece threadIdx.x & 15
+    const int lcol = threadIdx.x & 15;
+    const int rstep = NT / 16;
+    float4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
+#define KATTN_FETCH(K0)                                                                         \
+    {                                                                                           \
+        const int64_t r0 = min((K0) + lrow, n - 1), r1 = min((K0) + lrow + rstep, n - 1);       \
+        const int64_t r2 = min((K0) + lrow + 2 * rstep, n - 1), r3 = min((K0) + lrow + 3 * rstep, n - 1); \
+        pk0 = reinterpret_cast<const float4*>(kbase + r0 * p.k_stride)[lcol];                  \
+        pk1 = reinterpret_cast<const float4*>(kbase + r1 * p.k_stride)[lcol];                  \
+        pk2 = reinterpret_cast<const float4*>(kbase + r2 * p.k_stride)[lcol];                  \
+        pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];                  \
+        pv0 = reinterpret_cast<const float4*>(vbase + r0 * p.v_stride)[lcol];                  \
+        pv1 = reinterpret_cast<const float4*>(vbase + r1 * p.v_stride)[lcol];                  \
+        pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];                  \
+        pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];                  \
+    }
+#define KATTN_STASH()                                                                           \
+    {                                                                                           \
+        float* kd = &Ks[lrow * LDS_STRIDE + 4 * lcol];                                          \
+        float* vd = &Vs[lrow * LDS_STRIDE + 4 * lcol];                                          \
+        *reinterpret_cast<float4*>(kd) = pk0;                                                   \
+        *reinterpret_cast<float4*>(kd + rstep * LDS_STRIDE) = pk1;                              \
+        *reinterpret_cast<float4*>(kd + 2 * rstep * LDS_STRIDE) = pk2;                          \
+        *reinterpret_cast<float4*>(kd + 3 * rstep * LDS_STRIDE) = pk3;                          \
+        *reinterpret_cast<float4*>(vd) = pv0;                                                   \
+        *reinterpret_cast<float4*>(vd + rstep * LDS_STRIDE) = pv1;                              \
+        *reinterpret_cast<float4*>(vd + 2 * rstep * LDS_STRIDE) = pv2;                          \
+        *reinterpret_cast<float4*>(vd + 3 * rstep * LDS_STRIDE) = pv3;                          \
+    }
+    KATTN_FETCH(kbeg)
+    KATTN_STASH()
+    __syncthreads();
     for (int kt = kbeg; kt < kend; kt += BN) {
-        __syncthreads();  // the previous tile has been read by every wave
-        for (int idx = threadIdx.x; idx < BN * 16; idx += NT) {
-            const int r = idx >> 4, c = idx & 15;
-            const int key = kt + r;
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-            if (key < n) {
-                kv = reinterpret_cast<const float4*>(kbase + static_cast<int64_t>(key) * p.k_stride)[c];
-                vv = reinterpret_cast<const float4*>(vbase + static_cast<int64_t>(key) * p.v_stride)[c];
-            }
-            *reinterpret_cast<float4*>(&Ks[r * LDS_STRIDE + 4 * c]) = kv;
-            *reinterpret_cast<float4*>(&Vs[r * LDS_STRIDE + 4 * c]) = vv;
-        }
-        __syncthreads();
+        // the next tile's rows (the last trip re-reads this tile's, which are in cache)
+        KATTN_FETCH(min(kt + BN, kend - 1))
 
-        // Does this wave see any key of the tile, and all of them?
-        const int klast = kt + BN - 1;
-        bool any = wave_live && kt < n;
-        bool full = wave_live && klast < n;
-        if (p.causal) {
-            any = any && kt <= qlast_w;
-            full = full && klast <= qa;
-        }
-        if (p.hw >= 0) {
-            any = any && kt <= qlast_w + p.hw && klast >= qa - p.hw;
-            full = full && kt >= qlast_w - p.hw && klast <= qa + p.hw;
-        }
-        if (!any) continue;
-
-        // S^T = K Q^T for keys kt..kt+31 (S0) and kt+32..kt+63 (S1).
-        f32x16 S0, S1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            S0[r] = 0.0f;
-            S1[r] = 0.0f;
-        }
-        const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
-        const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
-            const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
-        }
-
-        if (!full) {
-            // boundary tile: masked scores become -inf (the same as skipping them)
+        // Which 32-key halves of the tile does this wave see (any key), and does it see
+        // every key of the tile?  Halves outside the wave's band are skipped outright.
+        auto sees = [&](int k0, int k1) {  // some key of [k0, k1] visible to some query
+            bool v = wave_live && k0 < n;
+            if (p.causal) v = v && k0 <= qlast_w;
+            if (p.hw >= 0) v = v && k0 <= qlast_w + p.hw && k1 >= qa - p.hw;
+            return v;
+        };
+        auto sees_all = [&](int k0, int k1) {  // every key of [k0, k1] visible to every query
+            bool v = wave_live && k1 < n;
+            if (p.causal) v = v && k1 <= qa;
+            if (p.hw >= 0) v = v && k0 >= qlast_w - p.hw && k1 <= qa + p.hw;
+            return v;
+        };
+        const bool use0 = sees(kt, kt + 31);
+        const bool use1 = BAND ? sees(kt + 32, kt + 63) : use0;
+        if (use0 && use1) {
+            const bool full = sees_all(kt, kt + BN - 1);
+            // S^T = K Q^T for keys kt..kt+31 (S0) and kt+32..kt+63 (S1).
+            f32x16 S0, S1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const int key1 = key0 + 32;
-                bool v0 = key0 < n, v1 = key1 < n;
-                if (p.causal) {
-                    v0 = v0 && key0 <= qi;
-                    v1 = v1 && key1 <= qi;
+                S0[r] = 0.0f;
+                S1[r] = 0.0f;
+            }
+            const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
+            const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
+                const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
+                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
+                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
+                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
+                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
+            }
+
+            if (!full) {
+                // boundary tile: masked scores become -inf (the same as skipping them)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const int key1 = key0 + 32;
+                    bool v0 = key0 < n, v1 = key1 < n;
+                    if (p.causal) {
+                        v0 = v0 && key0 <= qi;
+                        v1 = v1 && key1 <= qi;
+                    }
+                    if (p.hw >= 0) {
+                        v0 = v0 && abs(qi - key0) <= p.hw;
+                        v1 = v1 && abs(qi - key1) <= p.hw;
+                    }
+                    if (!v0) S0[r] = -INFINITY;
+                    if (!v1) S1[r] = -INFINITY;
                 }
-                if (p.hw >= 0) {
-                    v0 = v0 && abs(qi - key0) <= p.hw;
-                    v1 = v1 && abs(qi - key1) <= p.hw;
+            }
+
+            // online softmax
+            float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+            const float ml = m_new * kLog2e;
+            m_run = m_new;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
+                S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
+                psum += S0[r] + S1[r];
+            }
+            l_run = l_run * alpha + psum;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                O0[r] *= alpha;
+                O1[r] *= alpha;
+            }
+
+            // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
+                const float2 vb =
+                    *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
+                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
+                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
+                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
+                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
+            }
+        } else if (BAND && (use0 || use1)) {
+            // one half: the same steps on a single 32x32 score block
+            const int off = use0 ? 0 : 32;
+            const bool full = sees_all(kt + off, kt + off + 31);
+            f32x16 S;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = 0.0f;
+            const float* kr = &Ks[(off + j) * LDS_STRIDE + hh * 32];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 a = *reinterpret_cast<const float4*>(kr + 4 * m);
+                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qreg[4 * m + 0], S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qreg[4 * m + 1], S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qreg[4 * m + 2], S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qreg[4 * m + 3], S, 0, 0, 0);
+            }
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt + off + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    bool v = key < n;
+                    if (p.causal) v = v && key <= qi;
+                    if (p.hw >= 0) v = v && abs(qi - key) <= p.hw;
+                    if (!v) S[r] = -INFINITY;
                 }
-                if (!v0) S0[r] = -INFINITY;
-                if (!v1) S1[r] = -INFINITY;
+            }
+            float mx = S[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+            const float ml = m_new * kLog2e;
+            m_run = m_new;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], kLog2e, -ml));
+                psum += S[r];
+            }
+            l_run = l_run * alpha + psum;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                O0[r] *= alpha;
+                O1[r] *= alpha;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key0 = off + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
+                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S[r], O0, 0, 0, 0);
+                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S[r], O1, 0, 0, 0);
             }
         }
 
-        // online softmax
-        float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-        const float ml = m_new * kLog2e;
-        m_run = m_new;
-        float psum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
-            S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
-            psum += S0[r] + S1[r];
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            O0[r] *= alpha;
-            O1[r] *= alpha;
-        }
-
-        // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
-            const float2 vb =
-                *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
-            O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
-            O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
-            O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
-            O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
-        }
+        __syncthreads();  // every wave is done with this tile
+        if (kt + BN < kend) KATTN_STASH()
+        __syncthreads();
     }
+#undef KATTN_FETCH
+#undef KATTN_STASH
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (qi < n) {
@@ -386,7 +480,7 @@ Shape pick_shape(int R) {
     switch (R) {
         case 1: return {1, 4};
         case 2: return {2, 2};
-        case 3: return {1, 4};
+        case 3: return {1, 4};  // 3 heads x 32 rows would leave the 4 SIMDs unevenly loaded
         case 4: return {4, 1};
         default: return {1, 4};
     }
@@ -394,8 +488,12 @@ Shape pick_shape(int R) {
 
 template <int HPW, int QW>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<HPW, QW>), dim3(static_cast<unsigned>(grid)), dim3(64 * HPW * QW),
-                       0, stream, p);
+    if (p.causal || p.hw >= 0)
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * HPW * QW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * HPW * QW), 0, stream, p);
 }
 
 }  // namespace
@@ -493,7 +591,6 @@ extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, 
     p.scale = scale;
     if (sh.hpw == 1) launch_fwd<1, 4>(p, grid, stream);
     else if (sh.hpw == 2) launch_fwd<2, 2>(p, grid, stream);
-    else if (sh.hpw == 3) launch_fwd<3, 2>(p, grid, stream);
     else launch_fwd<4, 1>(p, grid, stream);
     return check_launch(fn);
 }
