@@ -130,6 +130,61 @@ def decode_part(torch, steps, warmup, flush):
     return res
 
 
+def traffic_from_profiles(workload: str, kernel_source: str):
+    """HBM bytes per launch measured with rocprofv3 PMC counters (profiles/traffic.json), or
+    None when the kernel source has changed since they were taken."""
+    import hashlib
+    from pathlib import Path
+    root = Path(__file__).resolve().parent
+    try:
+        rec = json.loads((root / "profiles" / "traffic.json").read_text())[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = root / "transformer_attention_varlen_amd" / "csrc" / kernel_source
+    if hashlib.sha256(src.read_bytes()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes"]
+
+
+def measure_ceilings(torch):
+    """Practical ceilings on this GPU, measured with library kernels: a cold 1 GiB read
+    (torch's sum) and a copy for HBM, a large FP32 GEMM (torch.mm) for the FP32 matrix units."""
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(buf)
+    other = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def best_ms(fn, reps=5):
+        out = []
+        for _ in range(reps):
+            sink.copy_(other.sum())  # evict buf from L2 / MALL
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out)
+
+    read_ms = best_ms(lambda: sink.copy_(buf.sum()))
+    copy_ms = best_ms(lambda: dst.copy_(buf))
+    n = 8192
+    A = torch.randn(n, n, device="cuda")
+    Bm = torch.randn(n, n, device="cuda")
+    C = torch.empty(n, n, device="cuda")
+    torch.mm(A, Bm, out=C)
+    gemm_ms = best_ms(lambda: torch.mm(A, Bm, out=C), reps=3)
+    res = {"hbm_read_gbs": round(buf.numel() * 4 / (read_ms * 1e-3) / 1e9, 1),
+           "hbm_copy_gbs": round(2 * buf.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
+           "fp32_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 2),
+           "how": "best of a few: torch sum over 1 GiB (cold), torch copy of 1 GiB, "
+                  "torch.mm 8192^3 FP32"}
+    del buf, dst, other, A, Bm, C
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, budget_s):
     """The oracle, untuned, on random samples of the workload's rows (all heads each),
     repeated until the time budget is spent."""
@@ -232,7 +287,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fwd_kernel (attention tile kernel)",
                      "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-                     "traffic": None, "mean_launch_ms": round(attn_ms, 4),
+                     "traffic": traffic_from_profiles(wl.WORKLOADS[HEADLINE].name, "prefill.hip"),
+                     "mean_launch_ms": round(attn_ms, 4),
                      "algorithmic_gflop_per_launch": round(flops / 1e9, 4)},
     }
     del run
@@ -250,6 +306,7 @@ def main():
                 parts[PARTS[k]] = prefill_part(torch, k, psteps, pwarm, flush)
         del flush
     out["parts"] = parts
+    out["ceilings"] = measure_ceilings(torch) if args.parts != "none" else None
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     else:

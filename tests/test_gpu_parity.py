@@ -266,3 +266,16 @@ def test_decode_skips_sequences_with_bad_lengths():
     out = run.out.cpu().numpy()
     assert np.all(out[1] == 7.0)
     assert np.array_equal(run.k_cache.cpu().numpy()[1], case.k_cache[1])
+
+
+def test_many_short_sequences_plan_beyond_lds():
+    # more sequences than the planner keeps in LDS: the tile prefix then lives in the workspace
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(0, 6, 5000)
+    lengths[rng.integers(0, 5000, 20)] = rng.integers(30, 140, 20)
+    case = wl.make_prefill(lengths, 4, 2, packed=False, window=-1, causal=True, seed=78)
+    run = gpu_prefill(case, pad_rows=3, sentinel=float("nan"))
+    got = run.out_full.cpu().numpy()
+    ref = oracle_prefill(case)
+    assert max_err(got[:case.T], ref) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))

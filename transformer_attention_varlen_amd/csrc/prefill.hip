@@ -51,8 +51,8 @@ constexpr int BN = 64;        // keys per LDS tile
 constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: exp2 of (-1e30 - m) is 0, never NaN
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanBins = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanBins = 1024;   // key-tile-count buckets (a multiple of kPlanThreads)
 
 // Workspace layout (bytes): [0,256) header (tile count), then the tile
 // prefix over sequences (S+1 ints), then the tile list (int2 each).
@@ -92,58 +92,82 @@ __device__ inline void key_range(int q0, int qend, int n, int hw, int causal, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// Planning kernel: one work-group of 1024 threads.
+// Planning kernel: one work-group of kPlanThreads threads lists the (sequence, first query
+// row) tiles, heaviest key range first.  Sequence lengths and the tile prefix live in LDS when
+// the batch has at most kPlanLdsSeqs sequences (the per-tile binary search then never touches
+// global memory); larger batches keep the prefix in the workspace.  Scans are wave-level with
+// one exchange between waves, so the whole plan takes a handful of barriers.
+constexpr int kPlanLdsSeqs = 4096;
+
+// Inclusive scan over the work-group; *total receives the sum of every thread's value.
+__device__ inline int block_scan(int v, int* wave_sums, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == 63) wave_sums[wave] = v;
+    __syncthreads();
+    int add = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+        add += w < wave ? wave_sums[w] : 0;
+        all += wave_sums[w];
+    }
+    __syncthreads();  // wave_sums may be reused
+    *total = all;
+    return v + add;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S,
                                                            int T, int BM, int hw, int causal,
                                                            int32_t* __restrict__ ws_prefix,
                                                            int2* __restrict__ tiles,
                                                            int32_t* __restrict__ count,
                                                            int64_t capacity) {
-    __shared__ int scan[kPlanThreads];
     __shared__ int hist[kPlanBins];
-    __shared__ int carry;
+    __shared__ int lds_pre[kPlanLdsSeqs + 1];
+    __shared__ int lds_len[kPlanLdsSeqs];
+    __shared__ int wave_sums[kPlanThreads / 64];
+    const bool in_lds = S <= kPlanLdsSeqs;
+    int* pre = in_lds ? lds_pre : ws_prefix;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        carry = 0;
-        ws_prefix[0] = 0;
-    }
-    // 1. tiles per sequence, inclusive prefix into ws_prefix[1..S]
-    for (int base = 0; base < S; base += kPlanThreads) {
-        const int s = base + tid;
-        int nt = 0;
-        if (s < S) {
-            const SeqRange r = seq_range(cu, s, T);
-            nt = (r.n + BM - 1) / BM;
-        }
-        scan[tid] = nt;
-        __syncthreads();
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
-            const int add = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
-        }
-        if (s < S) ws_prefix[s + 1] = carry + scan[tid];
-        __syncthreads();
-        if (tid == kPlanThreads - 1) carry += scan[tid];
-        __syncthreads();
+
+    // 1. tile counts of a contiguous run of sequences per thread, then their exclusive prefix
+    const int per = (S + kPlanThreads - 1) / kPlanThreads;
+    const int s0 = min(tid * per, S), s1 = min(s0 + per, S);
+    int mine = 0;
+    for (int s = s0; s < s1; ++s) {
+        const SeqRange r = seq_range(cu, s, T);
+        if (in_lds) lds_len[s] = r.n;
+        mine += (r.n + BM - 1) / BM;
     }
     for (int b = tid; b < kPlanBins; b += kPlanThreads) hist[b] = 0;
+    int all_tiles;
+    int run = block_scan(mine, wave_sums, &all_tiles) - mine;
+    for (int s = s0; s < s1; ++s) {
+        pre[s] = run;
+        run += ((in_lds ? lds_len[s] : seq_range(cu, s, T).n) + BM - 1) / BM;
+    }
+    if (tid == 0) pre[S] = all_tiles;
     __syncthreads();
-    const int total = static_cast<int>(min(static_cast<int64_t>(carry), capacity));
-    // 2. histogram of key-tile counts; 3. descending bucket offsets; 4. scatter
+    const int total = static_cast<int>(min(static_cast<int64_t>(all_tiles), capacity));
+
+    // 2. histogram of key-tile counts; 3. bucket offsets from the heaviest down; 4. scatter
+    constexpr int kBinsPer = kPlanBins / kPlanThreads;
     for (int pass = 0; pass < 2; ++pass) {
         for (int t = tid; t < total; t += kPlanThreads) {
-            int lo = 0, hi = S - 1;  // last s with ws_prefix[s] <= t
+            int lo = 0, hi = S - 1;  // last s with pre[s] <= t
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (ws_prefix[mid] <= t) lo = mid; else hi = mid - 1;
+                if (pre[mid] <= t) lo = mid; else hi = mid - 1;
             }
             const int s = lo;
-            const SeqRange r = seq_range(cu, s, T);
-            const int q0 = (t - ws_prefix[s]) * BM;
+            const int n = in_lds ? lds_len[s] : seq_range(cu, s, T).n;
+            const int q0 = (t - pre[s]) * BM;
             int kb, ke;
-            key_range(q0, min(q0 + BM, r.n), r.n, hw, causal, kb, ke);
+            key_range(q0, min(q0 + BM, n), n, hw, causal, kb, ke);
             const int work = ke > kb ? (ke - kb + BN - 1) / BN : 0;
             const int bin = min(work, kPlanBins - 1);
             if (pass == 0) {
@@ -155,19 +179,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         }
         __syncthreads();
         if (pass == 0) {
-            // exclusive scan over bins from the heaviest down
-            const int b = kPlanBins - 1 - tid;
-            scan[tid] = (tid < kPlanBins) ? hist[b] : 0;
-            __syncthreads();
-            for (int off = 1; off < kPlanThreads; off <<= 1) {
-                const int add = tid >= off ? scan[tid - off] : 0;
-                __syncthreads();
-                scan[tid] += add;
-                __syncthreads();
+            // thread tid owns bins kPlanBins-1-kBinsPer*tid-k, k < kBinsPer (heaviest first)
+            int cnt[kBinsPer], sum = 0;
+#pragma unroll
+            for (int k = 0; k < kBinsPer; ++k) {
+                cnt[k] = hist[kPlanBins - 1 - kBinsPer * tid - k];
+                sum += cnt[k];
             }
-            const int excl = scan[tid] - hist[b];
-            __syncthreads();
-            hist[b] = excl;
+            int unused;
+            int off = block_scan(sum, wave_sums, &unused) - sum;
+#pragma unroll
+            for (int k = 0; k < kBinsPer; ++k) {
+                hist[kPlanBins - 1 - kBinsPer * tid - k] = off;
+                off += cnt[k];
+            }
             __syncthreads();
         }
     }
