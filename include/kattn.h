@@ -125,7 +125,9 @@ size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T);
  *   q, k, v:    device float (T, H*64), (T, G*64), (T, G*64) with their own
  *               strides (a packed qkv row: k = q + H*64, v = k + G*64).
  *   cu:         device int32[S+1], the offsets of kattn_build_index.
- *   max_seqlen: longest sequence (host scalar, from kattn_build_index).
+ *   max_seqlen: longest sequence (host scalar, from kattn_build_index).  It must not
+ *               be smaller than the longest sequence: a window whose half-width reaches
+ *               max_seqlen - 1 masks nothing and runs as global attention.
  *   window:     -1 for none (the CUDA page's encoding), else >= 0.
  *   causal:     0 or 1.
  *   scale:      finite, > 0; folded into q as it is loaded (exact for 1/8).

@@ -47,7 +47,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 64;        // keys per LDS tile
+constexpr int BN = 64;        // key-range granularity of the planner's work estimate
 constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: exp2 of (-1e30 - m) is 0, never NaN
@@ -213,15 +213,19 @@ struct FwdParams {
     float scale;
 };
 
-// BAND: the launch has a window or a causal limit, so a wave may skip half tiles that fall
-// outside its band; without one (global attention) every half tile a wave reaches is live
-// except at a sequence's ragged end, and the single-half path is left out of the code.
-template <int HPW, int QW, bool BAND>
-__global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
+// TBN: keys per K/V tile.  Global launches use 64-key tiles (two 32-key score blocks per MFMA
+// round, fewer barriers per flop).  Banded launches (a window or a causal limit) use 32-key
+// tiles: a wave's band is covered with less waste, and half the score and staging registers
+// leave room for a third wave per SIMD.
+template <int HPW, int QW, int TBN>
+__global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(TBN == 32 ? 3 : 2)))
+void fwd_kernel(FwdParams p) {
+    static_assert(TBN == 32 || TBN == 64, "tiles hold one or two 32-key score blocks");
     constexpr int NT = 64 * HPW * QW;
     constexpr int BM = 32 * QW;
-    __shared__ __attribute__((aligned(16))) float Ks[BN * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) float Vs[BN * LDS_STRIDE];
+    constexpr bool TWO = TBN == 64;
+    __shared__ __attribute__((aligned(16))) float Ks[TBN * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) float Vs[TBN * LDS_STRIDE];
 
     const int tix = blockIdx.x / p.nunits;
     const int unit = blockIdx.x - tix * p.nunits;
@@ -270,6 +274,7 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
 
     int kbeg, kend;
     key_range(q0, min(q0 + BM, n), n, p.hw, p.causal, kbeg, kend);
+    kbeg = (kbeg / TBN) * TBN;
 
     const float* kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
     const float* vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
@@ -278,23 +283,26 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
     // before this tile's MFMA work and written to LDS after it, so the global-load latency
     // overlaps the compute.  Rows past the sequence are clamped to its last row (in bounds,
     // finite) and always masked: a tile holding them never takes the unmasked path.
-    static_assert(BN * 16 == 4 * NT, "each thread stages 4 pieces of K and 4 of V per tile");
-    const int lrow = threadIdx.x >> 4;  // rows lrow + 16i of the tile, piece threadIdx.x & 15
+    static_assert(TBN * 16 == (TWO ? 4 : 2) * NT, "each thread stages 2 or 4 pieces per tensor");
+    const int lrow = threadIdx.x >> 4;  // rows lrow + (NT/16)i of the tile, piece threadIdx.x & 15
     const int lcol = threadIdx.x & 15;
-    const int rstep = NT / 16;
+    constexpr int rstep = NT / 16;
     float4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
 #define KATTN_FETCH(K0)                                                                         \
     {                                                                                           \
         const int64_t r0 = min((K0) + lrow, n - 1), r1 = min((K0) + lrow + rstep, n - 1);       \
-        const int64_t r2 = min((K0) + lrow + 2 * rstep, n - 1), r3 = min((K0) + lrow + 3 * rstep, n - 1); \
         pk0 = reinterpret_cast<const float4*>(kbase + r0 * p.k_stride)[lcol];                  \
         pk1 = reinterpret_cast<const float4*>(kbase + r1 * p.k_stride)[lcol];                  \
-        pk2 = reinterpret_cast<const float4*>(kbase + r2 * p.k_stride)[lcol];                  \
-        pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];                  \
         pv0 = reinterpret_cast<const float4*>(vbase + r0 * p.v_stride)[lcol];                  \
         pv1 = reinterpret_cast<const float4*>(vbase + r1 * p.v_stride)[lcol];                  \
-        pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];                  \
-        pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];                  \
+        if constexpr (TWO) {                                                                    \
+            const int64_t r2 = min((K0) + lrow + 2 * rstep, n - 1);                             \
+            const int64_t r3 = min((K0) + lrow + 3 * rstep, n - 1);                             \
+            pk2 = reinterpret_cast<const float4*>(kbase + r2 * p.k_stride)[lcol];              \
+            pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];              \
+            pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];              \
+            pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];              \
+        }                                                                                       \
     }
 #define KATTN_STASH()                                                                           \
     {                                                                                           \
@@ -302,39 +310,36 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
         float* vd = &Vs[lrow * LDS_STRIDE + 4 * lcol];                                          \
         *reinterpret_cast<float4*>(kd) = pk0;                                                   \
         *reinterpret_cast<float4*>(kd + rstep * LDS_STRIDE) = pk1;                              \
-        *reinterpret_cast<float4*>(kd + 2 * rstep * LDS_STRIDE) = pk2;                          \
-        *reinterpret_cast<float4*>(kd + 3 * rstep * LDS_STRIDE) = pk3;                          \
         *reinterpret_cast<float4*>(vd) = pv0;                                                   \
         *reinterpret_cast<float4*>(vd + rstep * LDS_STRIDE) = pv1;                              \
-        *reinterpret_cast<float4*>(vd + 2 * rstep * LDS_STRIDE) = pv2;                          \
-        *reinterpret_cast<float4*>(vd + 3 * rstep * LDS_STRIDE) = pv3;                          \
+        if constexpr (TWO) {                                                                    \
+            *reinterpret_cast<float4*>(kd + 2 * rstep * LDS_STRIDE) = pk2;                      \
+            *reinterpret_cast<float4*>(kd + 3 * rstep * LDS_STRIDE) = pk3;                      \
+            *reinterpret_cast<float4*>(vd + 2 * rstep * LDS_STRIDE) = pv2;                      \
+            *reinterpret_cast<float4*>(vd + 3 * rstep * LDS_STRIDE) = pv3;                      \
+        }                                                                                       \
     }
     KATTN_FETCH(kbeg)
     KATTN_STASH()
     __syncthreads();
-    for (int kt = kbeg; kt < kend; kt += BN) {
+    for (int kt = kbeg; kt < kend; kt += TBN) {
         // the next tile's rows (the last trip re-reads this tile's, which are in cache)
-        KATTN_FETCH(min(kt + BN, kend - 1))
+        KATTN_FETCH(min(kt + TBN, kend - 1))
 
-        // Which 32-key halves of the tile does this wave see (any key), and does it see
-        // every key of the tile?  Halves outside the wave's band are skipped outright.
-        auto sees = [&](int k0, int k1) {  // some key of [k0, k1] visible to some query
-            bool v = wave_live && k0 < n;
-            if (p.causal) v = v && k0 <= qlast_w;
-            if (p.hw >= 0) v = v && k0 <= qlast_w + p.hw && k1 >= qa - p.hw;
-            return v;
-        };
-        auto sees_all = [&](int k0, int k1) {  // every key of [k0, k1] visible to every query
-            bool v = wave_live && k1 < n;
-            if (p.causal) v = v && k1 <= qa;
-            if (p.hw >= 0) v = v && k0 >= qlast_w - p.hw && k1 <= qa + p.hw;
-            return v;
-        };
-        const bool use0 = sees(kt, kt + 31);
-        const bool use1 = BAND ? sees(kt + 32, kt + 63) : use0;
-        if (use0 && use1) {
-            const bool full = sees_all(kt, kt + BN - 1);
-            // S^T = K Q^T for keys kt..kt+31 (S0) and kt+32..kt+63 (S1).
+        // Does this wave see some key of the tile, and does it see every one of them?
+        const int klast = kt + TBN - 1;
+        bool any = wave_live && kt < n;
+        bool full = wave_live && klast < n;
+        if (p.causal) {
+            any = any && kt <= qlast_w;
+            full = full && klast <= qa;
+        }
+        if (p.hw >= 0) {
+            any = any && kt <= qlast_w + p.hw && klast >= qa - p.hw;
+            full = full && kt >= qlast_w - p.hw && klast <= qa + p.hw;
+        }
+        if (any) {
+            // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
             f32x16 S0, S1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -346,15 +351,17 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
-                const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
                 S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
-                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
                 S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
-                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
                 S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
-                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
                 S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
-                S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
+                if constexpr (TWO) {
+                    const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
+                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
+                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
+                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
+                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
+                }
             }
 
             if (!full) {
@@ -373,14 +380,18 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
                         v1 = v1 && abs(qi - key1) <= p.hw;
                     }
                     if (!v0) S0[r] = -INFINITY;
-                    if (!v1) S1[r] = -INFINITY;
+                    if (TWO && !v1) S1[r] = -INFINITY;
                 }
             }
 
             // online softmax
-            float mx = fmaxf(S0[0], S1[0]);
+            float mx = S0[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+            if constexpr (TWO) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
@@ -390,8 +401,11 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
-                S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
-                psum += S0[r] + S1[r];
+                psum += S0[r];
+                if constexpr (TWO) {
+                    S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
+                    psum += S1[r];
+                }
             }
             l_run = l_run * alpha + psum;
 #pragma unroll
@@ -405,70 +419,19 @@ __global__ __launch_bounds__(64 * HPW * QW) void fwd_kernel(FwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
                 const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
-                const float2 vb =
-                    *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
                 O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
                 O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
-                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
-                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
-            }
-        } else if (BAND && (use0 || use1)) {
-            // one half: the same steps on a single 32x32 score block
-            const int off = use0 ? 0 : 32;
-            const bool full = sees_all(kt + off, kt + off + 31);
-            f32x16 S;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = 0.0f;
-            const float* kr = &Ks[(off + j) * LDS_STRIDE + hh * 32];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 a = *reinterpret_cast<const float4*>(kr + 4 * m);
-                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qreg[4 * m + 0], S, 0, 0, 0);
-                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qreg[4 * m + 1], S, 0, 0, 0);
-                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qreg[4 * m + 2], S, 0, 0, 0);
-                S = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qreg[4 * m + 3], S, 0, 0, 0);
-            }
-            if (!full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kt + off + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    bool v = key < n;
-                    if (p.causal) v = v && key <= qi;
-                    if (p.hw >= 0) v = v && abs(qi - key) <= p.hw;
-                    if (!v) S[r] = -INFINITY;
+                if constexpr (TWO) {
+                    const float2 vb =
+                        *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
+                    O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
+                    O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
                 }
-            }
-            float mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-            const float ml = m_new * kLog2e;
-            m_run = m_new;
-            float psum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], kLog2e, -ml));
-                psum += S[r];
-            }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                O0[r] *= alpha;
-                O1[r] *= alpha;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key0 = off + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
-                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S[r], O0, 0, 0, 0);
-                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S[r], O1, 0, 0, 0);
             }
         }
 
         __syncthreads();  // every wave is done with this tile
-        if (kt + BN < kend) KATTN_STASH()
+        if (kt + TBN < kend) KATTN_STASH()
         __syncthreads();
     }
 #undef KATTN_FETCH
@@ -514,10 +477,10 @@ Shape pick_shape(int R) {
 template <int HPW, int QW>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
     if (p.causal || p.hw >= 0)
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, true>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, false>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
 }
 
@@ -582,8 +545,9 @@ extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, 
     const int nunits = H / sh.hpw;
     const int64_t grid = capacity * nunits;
     if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
-    // half window; a window wider than the batch is the same as none of that width
-    const int hw = window < 0 ? -1 : std::min(window / 2, T);
+    // Half window.  A window that reaches across the longest sequence masks nothing, so it
+    // runs as global attention (the same kernel and the same bits as window = -1).
+    const int hw = (window < 0 || window / 2 >= max_seqlen - 1) ? -1 : window / 2;
 
     char* ws = static_cast<char*>(workspace);
     int32_t* count = reinterpret_cast<int32_t*>(ws);
