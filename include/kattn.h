@@ -143,8 +143,9 @@ int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_s
                      int32_t G, int32_t head_dim, int32_t window, int32_t causal, float scale,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace kattn_decode needs. */
-size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t max_used);
+/* Bytes of device workspace kattn_decode needs for B sequences, H q heads and G kv
+ * heads (0 for invalid sizes).  The size does not depend on the cache lengths. */
+size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G);
 
 /*
  * One decode step against preallocated caches ([argus text.rs] `KvAppend`,
@@ -167,8 +168,9 @@ size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t max_used);
  *   max_used:   host scalar, 1 <= max_used <= cap; sizes the split over keys.
  *   cos, sin:   device float[table_len][32] with table_len >= max_used, or
  *               both NULL when q and k_new are already rotated.
- *   workspace:  device, >= kattn_decode_workspace(B, H, max_used) bytes,
- *               256-byte aligned (per-chunk partial max, sum and output).
+ *   workspace:  device, >= kattn_decode_workspace(B, H, G) bytes, 256-byte
+ *               aligned (the key-split schedule and per-piece partial max, sum
+ *               and output).
  * B == 0 queues nothing.  Sequences whose used[b] is outside [1, max_used]
  * are skipped (their out row and caches are left untouched).
  * Errors: EINVAL, EUNSUPPORTED, EBOUNDS (max_used, cap, table_len,

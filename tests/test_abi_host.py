@@ -178,9 +178,12 @@ def test_decode_empty_batch_queues_nothing():
     assert _dec(B=0, out=None) == kattn.KATTN_OK
 
 
-def test_decode_workspace_covers_every_chunk():
-    small = kattn.kattn_decode_workspace(64, 9, 1)
-    big = kattn.kattn_decode_workspace(64, 9, 8192)
-    assert 0 < small < big
-    # per (sequence, chunk, q head): a 64-float partial output plus its max and sum
-    assert big >= 64 * 9 * (8192 // 256) * 66 * 4
+def test_decode_workspace_size():
+    a = kattn.kattn_decode_workspace(64, 9, 3)
+    b = kattn.kattn_decode_workspace(512, 9, 3)
+    assert 0 < a < b
+    # room for a partial (64-float output, max and sum) per q head of every piece: at most one
+    # piece per wave of the persistent grid plus one per (sequence, kv head) segment
+    assert a >= (8192 + 64 * 3) * 3 * 66 * 4
+    assert kattn.kattn_decode_workspace(64, 9, 2) == 0
+    assert kattn.kattn_decode_workspace(-1, 9, 3) == 0

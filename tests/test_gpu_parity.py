@@ -279,3 +279,13 @@ def test_many_short_sequences_plan_beyond_lds():
     ref = oracle_prefill(case)
     assert max_err(got[:case.T], ref) <= ATOL
     assert np.all(np.isnan(got[case.T:]))
+
+
+def test_decode_batch_beyond_one_launch():
+    # more sequences than one launch schedules: the host cuts the batch into launches
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 65, 1100).astype(np.int32)
+    lens[7] = 0  # an invalid length is skipped
+    case = _decode_case(lens, 4, 2, 64, seed=6)
+    case.used[7] = 1
+    _check_decode(case, rotate=True)

@@ -10,10 +10,13 @@
 // Design for gfx950: the step is HBM bound (each cached row is 256 bytes of
 // K and 256 of V, read once and used for every q head of its group).
 //
-// * Split over keys: a work-item is (sequence b, kv head g, chunk c of
-//   kChunk rows), one wave each.  Rows are read 4 per 16-byte load
-//   instruction (16 lanes per 256-byte row), so each instruction reads 1 KB
-//   of contiguous cache.
+// * Stream-K split over keys: the rows of all (sequence, kv head) segments,
+//   end to end, are cut into equal ranges, one per wave of a persistent grid
+//   sized to the GPU's resident capacity, so every wave streams the same
+//   number of rows and none waits in a tail.  A range that crosses segments
+//   leaves one partial per piece; the combine kernel merges the pieces.
+//   Rows are read 4 per 16-byte load instruction (16 lanes per 256-byte
+//   row), so each instruction reads 1 KB of contiguous cache.
 // * Per block of 32 rows the K rows go through LDS (XOR-swizzled 16-byte
 //   chunks, conflict-free both ways) so that each lane then scores one row:
 //   the softmax math (max, exp, sum) runs once per row instead of once per
@@ -23,11 +26,12 @@
 // * The append is fused: the work-item whose chunk holds row p = L-1 writes
 //   the rotated new key and the new value to the cache and substitutes them
 //   in registers for that row (no read-after-write through memory).
-// * A combine kernel merges the chunks of each (b, h) with the exact
+// * A combine kernel merges the pieces of each (b, h) with the exact
 //   log-sum-exp algebra and writes the output row.
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -35,7 +39,8 @@
 namespace kattn {
 namespace {
 
-constexpr int kChunk = 256;       // keys per split-K work-item
+constexpr int kMaxSeqs = 1024;    // sequences per launch: the schedule's prefix table is in LDS
+constexpr int kMaxWaves = 8192;   // persistent waves a launch may use (bounds the workspace)
 constexpr int kBlock = 32;        // keys scored together: one per lane of a half-wave
 constexpr int kWaves = 4;         // independent work-items per work-group (one per wave)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -76,9 +81,10 @@ struct DecParams {
     const int32_t* used;
     const float* cos_t;
     const float* sin_t;
-    float* part_o;   // [B][nch][H][64]
-    float* part_ml;  // [B][nch][H][2]
-    int cap, max_used, nch, chunk, B, H, G, R;
+    int32_t* ws_head;  // [0]: rows per wave; [1 .. B+1]: prefix of valid lengths over sequences
+    float* part_o;     // [piece][R][64]
+    float* part_ml;    // [piece][R][2]
+    int cap, max_used, waves, B, H, G, R;
     float scale;
 };
 
@@ -123,6 +129,39 @@ __device__ inline float halves_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Inclusive scan over a work-group of 64 * kWaves threads; *total gets the group's sum.
+__device__ inline int group_scan(int v, int* wave_sums, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == 63) wave_sums[wave] = v;
+    __syncthreads();
+    int add = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        add += w < wave ? wave_sums[w] : 0;
+        all += wave_sums[w];
+    }
+    __syncthreads();
+    *total = all;
+    return v + add;
+}
+
+// Valid length of sequence b (0 when used[b] is outside [1, max_used]).
+__device__ inline int valid_len(const DecParams& p, int b) {
+    const int L = p.used[b];
+    return (L >= 1 && L <= p.max_used) ? L : 0;
+}
+
+// Stream-K split: the rows of every (sequence, kv head) segment, laid end to end (sequence-
+// major, kv head minor), are cut into equal ranges, one per wave of a persistent grid sized
+// to the GPU's resident capacity, so every wave streams the same number of rows and the grid
+// drains together.  A range may cross segment boundaries; each (wave, segment) piece leaves
+// one partial (max, sum, o[64]) per q head, at piece id wave + segment (unique and increasing
+// along the rows).
 template <int R>
 __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) {
     // Per wave: K rows of the current block, 16-byte chunks XOR-swizzled by row so that both
@@ -131,162 +170,194 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
     __shared__ __attribute__((aligned(16))) float Ks_all[kWaves][kBlock * 64];
     __shared__ __attribute__((aligned(16))) float Qs_all[kWaves][R * 64];
     __shared__ __attribute__((aligned(16))) float Ps_all[kWaves][R * kBlock];
+    __shared__ int pre[kMaxSeqs + 1];  // prefix of valid lengths over sequences
+    __shared__ int wave_sums[kWaves];
     const int wave = threadIdx.x >> 6;
     float* Ks = Ks_all[wave];
     float* Qs = Qs_all[wave];
     float* Ps = Ps_all[wave];
-
-    // Work-items run chunk-major -- every (kv head, sequence) of chunk 0, then chunk 1, ... --
-    // so the items past a short sequence's end sit at the back of the grid.
-    const int item = blockIdx.x * kWaves + wave;
-    const int g = item % p.G;
-    const int b = (item / p.G) % p.B;
-    const int c = item / (p.G * p.B);
-    if (c >= p.nch) return;
-    const int L = p.used[b];
-    if (L < 1 || L > p.max_used) return;
-    const int c0 = c * p.chunk;
-    if (c0 >= L) return;
-    const int pnew = L - 1;
-    const int c1 = min(c0 + p.chunk, L);  // rows [c0, c1); row pnew comes from k_new / v_new
-    const bool owns_new = pnew < c1;
     const int lane = threadIdx.x & 63;
     const int t = lane & 15;    // staging / P.V layout: dims 4t..4t+3 ...
     const int grp = lane >> 4;  // ... of rows 4i + grp of the block
     const int j = lane & 31;    // scoring layout: row j of the block ...
     const int hf = lane >> 5;   // ... dims 32hf .. 32hf+31
 
-    for (int u = grp; u < R; u += 4) {
-        const float4 x =
-            rope4(p.q + (static_cast<int64_t>(b) * p.H + g * R + u) * 64, t, p.cos_t, p.sin_t, pnew);
-        *reinterpret_cast<float4*>(&Qs[u * 64 + 4 * t]) =
-            make_float4(x.x * p.scale, x.y * p.scale, x.z * p.scale, x.w * p.scale);
+    // prefix of valid lengths over the sequences (every work-group computes the same table)
+    const int per = (p.B + 64 * kWaves - 1) / (64 * kWaves);
+    const int b0 = min(static_cast<int>(threadIdx.x) * per, p.B), b1 = min(b0 + per, p.B);
+    int mine = 0;
+    for (int b = b0; b < b1; ++b) mine += valid_len(p, b);
+    int rows_per_head;
+    int run = group_scan(mine, wave_sums, &rows_per_head) - mine;
+    for (int b = b0; b < b1; ++b) {
+        pre[b] = run;
+        run += valid_len(p, b);
     }
+    if (threadIdx.x == 0) pre[p.B] = rows_per_head;
+    __syncthreads();
+    const int64_t total = static_cast<int64_t>(rows_per_head) * p.G;
+    const int64_t span = (total + p.waves - 1) / p.waves;  // rows per wave
+    if (blockIdx.x == 0) {  // the combine kernel reads the schedule back
+        for (int b = threadIdx.x; b <= p.B; b += 64 * kWaves) p.ws_head[1 + b] = pre[b];
+        if (threadIdx.x == 0) p.ws_head[0] = static_cast<int32_t>(span);
+    }
+    const int w = blockIdx.x * kWaves + wave;
+    int64_t r = static_cast<int64_t>(w) * span;
+    const int64_t r_end = min(r + span, total);
 
-    const int64_t head_off = (static_cast<int64_t>(b) * p.G + g) * p.cap;
-    const float4* kb = reinterpret_cast<const float4*>(p.k_cache + head_off * 64) + t;
-    const float4* vb = reinterpret_cast<const float4*>(p.v_cache + head_off * 64) + t;
-
-    // the appended row: rotated new key and new value, written to cache row pnew
-    float4 knew = make_float4(0.f, 0.f, 0.f, 0.f), vnew = knew;
-    if (owns_new) {
-        const int64_t kv_off = (static_cast<int64_t>(b) * p.G + g) * 64;
-        knew = rope4(p.k_new + kv_off, t, p.cos_t, p.sin_t, pnew);
-        vnew = reinterpret_cast<const float4*>(p.v_new + kv_off)[t];
-        if (grp == 0) {
-            reinterpret_cast<float4*>(p.k_cache + (head_off + pnew) * 64)[t] = knew;
-            reinterpret_cast<float4*>(p.v_cache + (head_off + pnew) * 64)[t] = vnew;
+    while (r < r_end) {
+        // the segment holding row r: the last sequence b with G * pre[b] <= r, then its kv head
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (static_cast<int64_t>(pre[mid]) * p.G <= r) lo = mid; else hi = mid - 1;
         }
-    }
+        const int b = lo;
+        const int L = pre[b + 1] - pre[b];
+        const int64_t seg_b = static_cast<int64_t>(pre[b]) * p.G;
+        const int g = static_cast<int>((r - seg_b) / L);
+        const int64_t seg = seg_b + static_cast<int64_t>(g) * L;
+        const int c0 = static_cast<int>(r - seg);
+        const int c1 = static_cast<int>(min(r_end - seg, static_cast<int64_t>(L)));  // rows [c0, c1)
+        r = seg + c1;
+        const int pnew = L - 1;  // row pnew comes from k_new / v_new
+        const bool owns_new = pnew < c1;
 
-    float m[R], lp[R];
-    float4 o[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        m[u] = kNegBig;
-        lp[u] = 0.0f;
-        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    for (int base = c0; base < c1; base += kBlock) {
-        // 1. K and V rows base + 4i + grp (clamped: always in bounds; extra rows are masked)
-        float4 kr[kBlock / 4], vr[kBlock / 4];
-#pragma unroll
-        for (int i = 0; i < kBlock / 4; ++i) {
-            const int r = min(base + 4 * i + grp, c1 - 1);
-            kr[i] = kb[static_cast<int64_t>(r) * 16];
-            vr[i] = vb[static_cast<int64_t>(r) * 16];
+        wave_sync();  // the previous piece is done with Qs
+        for (int u = grp; u < R; u += 4) {
+            const float4 x = rope4(p.q + (static_cast<int64_t>(b) * p.H + g * R + u) * 64, t,
+                                   p.cos_t, p.sin_t, pnew);
+            *reinterpret_cast<float4*>(&Qs[u * 64 + 4 * t]) =
+                make_float4(x.x * p.scale, x.y * p.scale, x.z * p.scale, x.w * p.scale);
         }
-        if (owns_new && base + kBlock > pnew) {  // the block holding the new row
+
+        const int64_t head_off = (static_cast<int64_t>(b) * p.G + g) * p.cap;
+        const float4* kb = reinterpret_cast<const float4*>(p.k_cache + head_off * 64) + t;
+        const float4* vb = reinterpret_cast<const float4*>(p.v_cache + head_off * 64) + t;
+
+        // the appended row: rotated new key and new value, written to cache row pnew
+        float4 knew = make_float4(0.f, 0.f, 0.f, 0.f), vnew = knew;
+        if (owns_new) {
+            const int64_t kv_off = (static_cast<int64_t>(b) * p.G + g) * 64;
+            knew = rope4(p.k_new + kv_off, t, p.cos_t, p.sin_t, pnew);
+            vnew = reinterpret_cast<const float4*>(p.v_new + kv_off)[t];
+            if (grp == 0) {
+                reinterpret_cast<float4*>(p.k_cache + (head_off + pnew) * 64)[t] = knew;
+                reinterpret_cast<float4*>(p.v_cache + (head_off + pnew) * 64)[t] = vnew;
+            }
+        }
+
+        float m[R], lp[R];
+        float4 o[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            m[u] = kNegBig;
+            lp[u] = 0.0f;
+            o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+
+        for (int base = c0; base < c1; base += kBlock) {
+            // 1. K and V rows base + 4i + grp (clamped: always in bounds; extras are masked)
+            float4 kr[kBlock / 4], vr[kBlock / 4];
 #pragma unroll
             for (int i = 0; i < kBlock / 4; ++i) {
-                if (base + 4 * i + grp == pnew) {
-                    kr[i] = knew;
-                    vr[i] = vnew;
+                const int rr = min(base + 4 * i + grp, c1 - 1);
+                kr[i] = kb[static_cast<int64_t>(rr) * 16];
+                vr[i] = vb[static_cast<int64_t>(rr) * 16];
+            }
+            if (owns_new && base + kBlock > pnew) {  // the block holding the new row
+#pragma unroll
+                for (int i = 0; i < kBlock / 4; ++i) {
+                    if (base + 4 * i + grp == pnew) {
+                        kr[i] = knew;
+                        vr[i] = vnew;
+                    }
                 }
             }
-        }
-        wave_sync();  // the previous block's reads of Ks / Ps are done
-#pragma unroll
-        for (int i = 0; i < kBlock / 4; ++i) {
-            const int row = 4 * i + grp;
-            *reinterpret_cast<float4*>(&Ks[row * 64 + 4 * (t ^ (row & 15))]) = kr[i];
-        }
-        wave_sync();
-
-        // 2. scores: lane (hf, j) dots row j over dims 32hf..32hf+31, halves then summed.
-        // q is read from LDS each block: an opaque offset keeps the compiler from hoisting
-        // the 32R loop-invariant reads into registers (which would cost occupancy).
-        int qoff = 0;
-        asm volatile("" : "+s"(qoff));
-        qoff &= ~3;  // keeps the 16-byte alignment visible, so q is read as ds_read_b128
-        float s[R];
-#pragma unroll
-        for (int u = 0; u < R; ++u) s[u] = 0.0f;
-#pragma unroll 2
-        for (int cc = 0; cc < 8; ++cc) {
-            const int chunk = 8 * hf + cc;
-            const float4 kk = *reinterpret_cast<const float4*>(&Ks[j * 64 + 4 * (chunk ^ (j & 15))]);
-#pragma unroll
-            for (int u = 0; u < R; ++u) {
-                const float4 qq = *reinterpret_cast<const float4*>(&Qs[qoff + u * 64 + 4 * chunk]);
-                s[u] = __builtin_fmaf(kk.x, qq.x, s[u]);
-                s[u] = __builtin_fmaf(kk.y, qq.y, s[u]);
-                s[u] = __builtin_fmaf(kk.z, qq.z, s[u]);
-                s[u] = __builtin_fmaf(kk.w, qq.w, s[u]);
-            }
-        }
-        const bool valid = base + j < c1;
-
-        // 3. online softmax over the block's 32 rows (both halves hold the same values)
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const float sv = valid ? halves_sum(s[u]) : -INFINITY;
-            const float mx = pair_rows_max(row_max16(sv));
-            const float m_new = fmaxf(m[u], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m[u] - m_new) * kLog2e);
-            const float pu = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kLog2e, -m_new * kLog2e));
-            m[u] = m_new;
-            lp[u] = __builtin_fmaf(lp[u], alpha, pu);
-            o[u] = make_float4(o[u].x * alpha, o[u].y * alpha, o[u].z * alpha, o[u].w * alpha);
-            // row j = 4i + grp' goes to slot grp'*8 + i, so a P.V lane reads 8 in a row
-            if (hf == 0) Ps[u * kBlock + (j & 3) * (kBlock / 4) + (j >> 2)] = pu;
-        }
-        wave_sync();
-
-        // 4. O += P V over the block
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const float4 pa = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8]);
-            const float4 pb = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8 + 4]);
-            const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-            float4 acc = o[u];
+            wave_sync();  // the previous block's reads of Ks / Ps are done
 #pragma unroll
             for (int i = 0; i < kBlock / 4; ++i) {
-                acc.x = __builtin_fmaf(pw[i], vr[i].x, acc.x);
-                acc.y = __builtin_fmaf(pw[i], vr[i].y, acc.y);
-                acc.z = __builtin_fmaf(pw[i], vr[i].z, acc.z);
-                acc.w = __builtin_fmaf(pw[i], vr[i].w, acc.w);
+                const int row = 4 * i + grp;
+                *reinterpret_cast<float4*>(&Ks[row * 64 + 4 * (t ^ (row & 15))]) = kr[i];
             }
-            o[u] = acc;
-        }
-    }
+            wave_sync();
 
-    // the chunk's partials: max (uniform), sum over the 32 rows, output summed over the 4 groups
+            // 2. scores: lane (hf, j) dots row j over dims 32hf..32hf+31, halves then summed.
+            // q is read from LDS each block: an opaque offset keeps the compiler from hoisting
+            // the 32R loop-invariant reads into registers (which would cost occupancy).
+            int qoff = 0;
+            asm volatile("" : "+s"(qoff));
+            qoff &= ~3;  // keeps the 16-byte alignment visible, so q is read as ds_read_b128
+            float sc[R];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-        // lanes 0-31 hold one copy of each row's sum (lanes 32-63 repeat them)
-        const float l = halves_sum(pair_rows_sum(row_sum16(hf == 0 ? lp[u] : 0.0f)));
-        float4 acc = o[u];
-        acc.x = halves_sum(pair_rows_sum(acc.x));
-        acc.y = halves_sum(pair_rows_sum(acc.y));
-        acc.z = halves_sum(pair_rows_sum(acc.z));
-        acc.w = halves_sum(pair_rows_sum(acc.w));
-        const int64_t slot = (static_cast<int64_t>(b) * p.nch + c) * p.H + g * R + u;
-        if (grp == 0) reinterpret_cast<float4*>(p.part_o + slot * 64)[t] = acc;
-        if (lane == 0) {
-            p.part_ml[slot * 2 + 0] = m[u];
-            p.part_ml[slot * 2 + 1] = l;
+            for (int u = 0; u < R; ++u) sc[u] = 0.0f;
+#pragma unroll 2
+            for (int cc = 0; cc < 8; ++cc) {
+                const int chunk = 8 * hf + cc;
+                const float4 kk =
+                    *reinterpret_cast<const float4*>(&Ks[j * 64 + 4 * (chunk ^ (j & 15))]);
+#pragma unroll
+                for (int u = 0; u < R; ++u) {
+                    const float4 qq = *reinterpret_cast<const float4*>(&Qs[qoff + u * 64 + 4 * chunk]);
+                    sc[u] = __builtin_fmaf(kk.x, qq.x, sc[u]);
+                    sc[u] = __builtin_fmaf(kk.y, qq.y, sc[u]);
+                    sc[u] = __builtin_fmaf(kk.z, qq.z, sc[u]);
+                    sc[u] = __builtin_fmaf(kk.w, qq.w, sc[u]);
+                }
+            }
+            const bool valid = base + j < c1;
+
+            // 3. online softmax over the block's 32 rows (both halves hold the same values)
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float sv = valid ? halves_sum(sc[u]) : -INFINITY;
+                const float mx = pair_rows_max(row_max16(sv));
+                const float m_new = fmaxf(m[u], mx);
+                const float alpha = __builtin_amdgcn_exp2f((m[u] - m_new) * kLog2e);
+                const float pu = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kLog2e, -m_new * kLog2e));
+                m[u] = m_new;
+                lp[u] = __builtin_fmaf(lp[u], alpha, pu);
+                o[u] = make_float4(o[u].x * alpha, o[u].y * alpha, o[u].z * alpha, o[u].w * alpha);
+                // row j = 4i + grp' goes to slot grp'*8 + i, so a P.V lane reads 8 in a row
+                if (hf == 0) Ps[u * kBlock + (j & 3) * (kBlock / 4) + (j >> 2)] = pu;
+            }
+            wave_sync();
+
+            // 4. O += P V over the block
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float4 pa = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8]);
+                const float4 pb = *reinterpret_cast<const float4*>(&Ps[u * kBlock + grp * 8 + 4]);
+                const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                float4 acc = o[u];
+#pragma unroll
+                for (int i = 0; i < kBlock / 4; ++i) {
+                    acc.x = __builtin_fmaf(pw[i], vr[i].x, acc.x);
+                    acc.y = __builtin_fmaf(pw[i], vr[i].y, acc.y);
+                    acc.z = __builtin_fmaf(pw[i], vr[i].z, acc.z);
+                    acc.w = __builtin_fmaf(pw[i], vr[i].w, acc.w);
+                }
+                o[u] = acc;
+            }
+        }
+
+        // the piece's partials: max (uniform), sum over the rows, output summed over the groups
+        const int64_t piece = static_cast<int64_t>(w) + static_cast<int64_t>(b) * p.G + g;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            // lanes 0-31 hold one copy of each row's sum (lanes 32-63 repeat them)
+            const float l = halves_sum(pair_rows_sum(row_sum16(hf == 0 ? lp[u] : 0.0f)));
+            float4 acc = o[u];
+            acc.x = halves_sum(pair_rows_sum(acc.x));
+            acc.y = halves_sum(pair_rows_sum(acc.y));
+            acc.z = halves_sum(pair_rows_sum(acc.z));
+            acc.w = halves_sum(pair_rows_sum(acc.w));
+            const int64_t slot = piece * R + u;
+            if (grp == 0) reinterpret_cast<float4*>(p.part_o + slot * 64)[t] = acc;
+            if (lane == 0) {
+                p.part_ml[slot * 2 + 0] = m[u];
+                p.part_ml[slot * 2 + 1] = l;
+            }
         }
     }
 }
@@ -302,29 +373,33 @@ __device__ inline float wave_sum(float x) {
     return x;
 }
 
-// One wave per (q head, sequence): lanes take chunks for the max and the sum, then
-// output dims for the weighted sum of the chunks' partial outputs (8 loads in flight).
+// One wave per (q head, sequence): the pieces of its segment are the waves whose row
+// ranges overlap it.  Lanes take pieces for the max and the sum, then output dims for the
+// weighted sum of the pieces' partial outputs (8 loads in flight).
 __global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ out,
                                                             const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
-                                                            const int32_t* __restrict__ used,
-                                                            int max_used, int nch, int H,
-                                                            int chunk) {
+                                                            const int32_t* __restrict__ ws_head,
+                                                            int G, int H) {
     const int h = blockIdx.x, b = blockIdx.y;
-    const int L = used[b];
-    if (L < 1 || L > max_used) return;
-    const int nc = (L + chunk - 1) / chunk;
+    const int R = H / G, g = h / R, u = h % R;
+    const int64_t span = ws_head[0];
+    const int pb = ws_head[1 + b], L = ws_head[2 + b] - pb;
+    if (L < 1) return;  // not a valid sequence: nothing was computed
+    const int64_t seg = static_cast<int64_t>(pb) * G + static_cast<int64_t>(g) * L;
+    const int64_t w0 = seg / span, w1 = (seg + L - 1) / span;
+    const int nc = static_cast<int>(w1 - w0 + 1);
+    const int64_t piece0 = w0 + static_cast<int64_t>(b) * G + g;  // piece of wave w0 + i: piece0 + i
     const int lane = threadIdx.x;
-    const int64_t base = static_cast<int64_t>(b) * nch * H + h;  // slot of chunk c: base + c*H
     float mloc = kNegBig;
-    for (int c = lane; c < nc; c += 64) mloc = fmaxf(mloc, part_ml[(base + static_cast<int64_t>(c) * H) * 2]);
+    for (int c = lane; c < nc; c += 64) mloc = fmaxf(mloc, part_ml[((piece0 + c) * R + u) * 2]);
     const float M = wave_max(mloc);
     float lsum = 0.0f, acc = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += 64) {
         const int c = c0 + lane;
         float f = 0.0f;
         if (c < nc) {
-            const int64_t slot = base + static_cast<int64_t>(c) * H;
+            const int64_t slot = (piece0 + c) * R + u;
             f = __builtin_amdgcn_exp2f((part_ml[slot * 2] - M) * kLog2e);
             lsum = __builtin_fmaf(part_ml[slot * 2 + 1], f, lsum);
         }
@@ -334,7 +409,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ 
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int ci = c0 + min(i0 + k, n - 1);
-                v[k] = part_o[(base + static_cast<int64_t>(ci) * H) * 64 + lane];
+                v[k] = part_o[((piece0 + ci) * R + u) * 64 + lane];
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -348,16 +423,60 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ 
 }
 
 template <int R>
-void launch_split(const DecParams& p, int B, hipStream_t stream) {
-    const int64_t items = static_cast<int64_t>(p.nch) * B * p.G;
-    hipLaunchKernelGGL((decode_split_kernel<R>), dim3(static_cast<unsigned>((items + kWaves - 1) / kWaves)),
-                       dim3(64 * kWaves), 0, stream, p);
+const void* split_kernel_ptr() {
+    return reinterpret_cast<const void*>(&decode_split_kernel<R>);
 }
 
-size_t part_bytes(int32_t B, int32_t H, int32_t nch) {
-    const size_t slots = static_cast<size_t>(B) * nch * H;
-    const size_t o = (slots * 64 * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    return o + slots * 2 * sizeof(float);
+const void* split_kernel_for(int R) {
+    switch (R) {
+        case 1: return split_kernel_ptr<1>();
+        case 2: return split_kernel_ptr<2>();
+        case 3: return split_kernel_ptr<3>();
+        case 4: return split_kernel_ptr<4>();
+        case 5: return split_kernel_ptr<5>();
+        case 6: return split_kernel_ptr<6>();
+        case 7: return split_kernel_ptr<7>();
+        default: return split_kernel_ptr<8>();
+    }
+}
+
+// Waves of the split kernel the current device holds at once (its resident capacity), cached
+// per device and R; the persistent grid is sized to it.
+int resident_waves(int R, int* waves) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cache[kMaxDevices][kMaxR + 1] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KATTN_EDEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < kMaxDevices && cache[dev][R] > 0) {
+        *waves = cache[dev][R];
+        return KATTN_OK;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_for(R), 64 * kWaves, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return KATTN_EDEVICE;
+    const int w = std::min(kMaxWaves, std::max(1, per_cu) * std::max(1, cus) * kWaves);
+    if (dev >= 0 && dev < kMaxDevices) cache[dev][R] = w;
+    *waves = w;
+    return KATTN_OK;
+}
+
+struct WsLayout {
+    size_t head, part_o, part_ml, total;
+};
+WsLayout ws_layout(int32_t B, int32_t H, int32_t G) {
+    const size_t align = 255;
+    const int32_t bs = std::min(B, kMaxSeqs);
+    const size_t slots = (static_cast<size_t>(kMaxWaves) + static_cast<size_t>(bs) * G) * (H / G);
+    WsLayout l;
+    l.head = 0;
+    l.part_o = ((static_cast<size_t>(kMaxSeqs) + 2) * sizeof(int32_t) + align) & ~align;
+    l.part_ml = l.part_o + ((slots * 64 * sizeof(float) + align) & ~align);
+    l.total = l.part_ml + slots * 2 * sizeof(float);
+    return l;
 }
 
 }  // namespace
@@ -365,10 +484,9 @@ size_t part_bytes(int32_t B, int32_t H, int32_t nch) {
 
 using namespace kattn;
 
-extern "C" size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t max_used) {
-    if (B < 0 || H < 1 || max_used < 0) return 0;
-    const int32_t nch = (max_used + kChunk - 1) / kChunk;
-    return part_bytes(B, H, nch);
+extern "C" size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G) {
+    if (B < 0 || H < 1 || G < 1 || H % G != 0) return 0;
+    return ws_layout(B, H, G).total;
 }
 
 extern "C" int kattn_decode(float* out, const float* q, const float* k_new, const float* v_new,
@@ -383,6 +501,7 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     if (H % G != 0) return fail(KATTN_EUNSUPPORTED, "%s: H=%d is not a multiple of G=%d", fn, H, G);
     if (H / G > kMaxR)
         return fail(KATTN_EUNSUPPORTED, "%s: %d q heads per kv head (at most %d)", fn, H / G, kMaxR);
+    if (H > 65535) return fail(KATTN_EUNSUPPORTED, "%s: H=%d above the grid limit", fn, H);
     if (!(scale > 0.0f) || !std::isfinite(scale))
         return fail(KATTN_EINVAL, "%s: scale must be finite and > 0", fn);
     if (cap < 1) return fail(KATTN_EINVAL, "%s: cap %d < 1", fn, cap);
@@ -400,9 +519,11 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
         return fail(KATTN_EUNSUPPORTED, "%s: pointers must be multiples of 16 bytes", fn);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
-    const size_t need = kattn_decode_workspace(B, H, max_used);
-    if (workspace_bytes < need)
-        return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+    const WsLayout lay = ws_layout(B, H, G);
+    if (workspace_bytes < lay.total)
+        return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, lay.total);
+    if (static_cast<int64_t>(max_used) * G * std::min(B, kMaxSeqs) >= 0x7fffffff)
+        return fail(KATTN_EBOUNDS, "%s: rows of one launch exceed 2^31", fn);
     if (debug_checks()) {
         std::vector<int32_t> h(B);
         if (hipMemcpy(h.data(), used, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess)
@@ -411,45 +532,54 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
             if (h[i] < 1 || h[i] > max_used)
                 return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [1, max_used=%d]", fn, i, h[i], max_used);
     }
-    const int32_t nch = (max_used + kChunk - 1) / kChunk;
-    if (B > 65535 || static_cast<int64_t>(nch) * B * G / kWaves >= 0x7fffffff)
-        return fail(KATTN_EBOUNDS, "%s: batch above the grid limit", fn);
+    const int R = H / G;
+    int waves = 0;
+    if (resident_waves(R, &waves) != KATTN_OK)
+        return fail(KATTN_EDEVICE, "%s: occupancy query failed", fn);
+    waves -= waves % kWaves;
 
-    DecParams p;
-    p.q = q;
-    p.k_new = k_new;
-    p.v_new = v_new;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.used = used;
-    p.cos_t = cos;
-    p.sin_t = sin;
     char* ws = static_cast<char*>(workspace);
-    const size_t slots = static_cast<size_t>(B) * nch * H;
-    p.part_o = reinterpret_cast<float*>(ws);
-    p.part_ml = reinterpret_cast<float*>(ws + ((slots * 64 * sizeof(float) + 255) & ~static_cast<size_t>(255)));
-    p.cap = cap;
-    p.max_used = max_used;
-    p.nch = nch;
-    p.chunk = kChunk;
-    p.B = B;
-    p.H = H;
-    p.G = G;
-    p.R = H / G;
-    p.scale = scale;
-    switch (p.R) {
-        case 1: launch_split<1>(p, B, stream); break;
-        case 2: launch_split<2>(p, B, stream); break;
-        case 3: launch_split<3>(p, B, stream); break;
-        case 4: launch_split<4>(p, B, stream); break;
-        case 5: launch_split<5>(p, B, stream); break;
-        case 6: launch_split<6>(p, B, stream); break;
-        case 7: launch_split<7>(p, B, stream); break;
-        default: launch_split<8>(p, B, stream); break;
+    // sequences are taken kMaxSeqs at a time (the schedule's prefix table lives in LDS)
+    for (int32_t s0 = 0; s0 < B; s0 += kMaxSeqs) {
+        const int32_t bs = std::min(kMaxSeqs, B - s0);
+        DecParams p;
+        p.q = q + static_cast<int64_t>(s0) * H * 64;
+        p.k_new = k_new + static_cast<int64_t>(s0) * G * 64;
+        p.v_new = v_new + static_cast<int64_t>(s0) * G * 64;
+        p.k_cache = k_cache + static_cast<int64_t>(s0) * G * cap * 64;
+        p.v_cache = v_cache + static_cast<int64_t>(s0) * G * cap * 64;
+        p.used = used + s0;
+        p.cos_t = cos;
+        p.sin_t = sin;
+        p.ws_head = reinterpret_cast<int32_t*>(ws + lay.head);
+        p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+        p.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
+        p.cap = cap;
+        p.max_used = max_used;
+        p.waves = waves;
+        p.B = bs;
+        p.H = H;
+        p.G = G;
+        p.R = R;
+        p.scale = scale;
+        const dim3 grid(waves / kWaves), block(64 * kWaves);
+        switch (R) {
+            case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, p); break;
+            case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, p); break;
+            case 3: hipLaunchKernelGGL(decode_split_kernel<3>, grid, block, 0, stream, p); break;
+            case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, p); break;
+            case 5: hipLaunchKernelGGL(decode_split_kernel<5>, grid, block, 0, stream, p); break;
+            case 6: hipLaunchKernelGGL(decode_split_kernel<6>, grid, block, 0, stream, p); break;
+            case 7: hipLaunchKernelGGL(decode_split_kernel<7>, grid, block, 0, stream, p); break;
+            default: hipLaunchKernelGGL(decode_split_kernel<8>, grid, block, 0, stream, p); break;
+        }
+        int rc = check_launch(fn);
+        if (rc != KATTN_OK) return rc;
+        hipLaunchKernelGGL(decode_combine_kernel, dim3(H, bs), dim3(64), 0, stream,
+                           out + static_cast<int64_t>(s0) * H * 64, p.part_o, p.part_ml, p.ws_head,
+                           G, H);
+        rc = check_launch(fn);
+        if (rc != KATTN_OK) return rc;
     }
-    int rc = check_launch(fn);
-    if (rc != KATTN_OK) return rc;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(H, B), dim3(64), 0, stream, out, p.part_o,
-                       p.part_ml, used, max_used, nch, H, p.chunk);
-    return check_launch(fn);
+    return ok();
 }

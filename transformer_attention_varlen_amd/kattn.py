@@ -117,8 +117,8 @@ def kattn_varlen_fwd_workspace(S: int, T: int) -> int:
     return int(lib().kattn_varlen_fwd_workspace(int(S), int(T)))
 
 
-def kattn_decode_workspace(B: int, H: int, max_used: int) -> int:
-    return int(lib().kattn_decode_workspace(int(B), int(H), int(max_used)))
+def kattn_decode_workspace(B: int, H: int, G: int) -> int:
+    return int(lib().kattn_decode_workspace(int(B), int(H), int(G)))
 
 
 # ----------------------------------------------------------------------------- device calls

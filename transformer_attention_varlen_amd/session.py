@@ -106,7 +106,7 @@ class DecodeRun:
         else:
             self.cos = self.sin = None
         self.out = torch.empty((case.B, case.H * HEAD_DIM), dtype=torch.float32, device=device)
-        ws = kattn.kattn_decode_workspace(case.B, case.H, self.max_used)
+        ws = kattn.kattn_decode_workspace(case.B, case.H, case.G)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
 
     def step(self):
