@@ -3,8 +3,11 @@
 
 Prints ONE JSON line.  A step is one pass of the hot path over the headline
 workload (ModernBERT-base local layer: 64 packed sequences of U[16,512]
-tokens, 12 heads, window 128, RoPE theta 1e4): the RoPE prologue then the
-attention forward, inputs resident in HBM.  The same line carries the other
+tokens, 12 heads, window 128, RoPE theta 1e4), inputs resident in HBM:
+the attention forward with the RoPE step fused into its tile loads
+(kattn_varlen_fwd_rope: the tile planner, then the tile kernel, which rotates
+q and k as it loads them).  The two-pass form of the same step (in-place RoPE
+prologue, then kattn_varlen_fwd) is timed beside it.  The same line carries the other
 workloads of the path, each timed per call with HIP events on the stream it
 runs on and the L2/MALL flushed between calls:
 
@@ -48,6 +51,8 @@ def parse():
                     help="budget for the CPU oracle baseline (0 disables)")
     ap.add_argument("--only", default=None,
                     help="run only this workload's loop (for profiling): 1, 2, 3a, 3b or 4")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --only: loop the fused-RoPE step instead of prologue + attention")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="with --only: also run one plain device copy of this many MiB, the "
                          "known-size kernel that scales PMC byte counters")
@@ -93,6 +98,12 @@ def prefill_part(torch, key, steps, warmup, flush):
     from transformer_attention_varlen_amd.session import PrefillRun
     case = wl.build(key)
     run = PrefillRun(case)
+    # fused first, on the unrotated inputs; then the prologue and the two-pass attention
+    fused_ms, _ = time_calls(torch, run.attention_rope, steps, warmup, flush)
+    out16 = torch.empty((case.T, case.H * 64), dtype=torch.float16, device="cuda")
+    f16_ms, _ = time_calls(torch, lambda: run.attention_f16(out16, fused=True),
+                           max(3, steps // 2), 1, flush)
+    del out16
     run.rope()
     mean_ms, min_ms = time_calls(torch, run.attention, steps, warmup, flush)
     rope_ms, _ = time_calls(torch, run.rope, max(3, steps // 4), 1, flush)
@@ -106,7 +117,10 @@ def prefill_part(torch, key, steps, warmup, flush):
            "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
            "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
            "rope_ms": round(rope_ms, 4),
-           "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1)}
+           "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1),
+           "fused_rope_attn_ms": round(fused_ms, 4),
+           "fused_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+           "fused_f16_out_ms": round(f16_ms, 4)}
     del run
     torch.cuda.empty_cache()
     return res
@@ -236,7 +250,7 @@ def main():
             fn = run.step
         else:
             run = PrefillRun(wl.build(args.only))
-            fn = run.step
+            fn = run.step_fused if args.fused else run.step
         for _ in range(args.warmup + args.steps):
             fn()
         torch.cuda.synchronize()
@@ -253,23 +267,31 @@ def main():
 
     case = wl.build(HEADLINE)
     run = PrefillRun(case)
-    # warmup, then K timed steps bracketed by synchronisation; the attention launch of each
-    # step is also bracketed by events on the stream it is queued on
+    # warmup, then K timed steps bracketed by synchronisation; each step's launches (planner,
+    # tile kernel) are also bracketed by events on the stream they are queued on
     for _ in range(args.warmup):
-        run.step()
+        run.step_fused()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in evs:
-        run.rope()
         a.record()
-        run.attention()
+        run.step_fused()
         b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     ms_per_step = wall * 1e3 / args.steps
+    # the two-pass form of the same step: in-place RoPE prologue, then attention
+    for _ in range(2):
+        run.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step()
+    torch.cuda.synchronize()
+    two_pass_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     value = case.T / (ms_per_step * 1e-3) / 1e6
@@ -283,8 +305,10 @@ def main():
                    "heads": case.H, "kv_heads": case.G, "head_dim": 64, "window": case.window,
                    "causal": case.causal, "rope_theta": case.theta,
                    "seed": wl.WORKLOADS[HEADLINE].seed,
-                   "step": "rope prologue + attention forward"},
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel (attention tile kernel)",
+                   "step": "attention forward with RoPE fused into the tile loads",
+                   "two_pass_ms_per_step": round(two_pass_ms, 4)},
+        "roofline": {"bound": "mfma",
+                     "kernel": "fwd_kernel, fused-RoPE variant (events span the planner too)",
                      "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": traffic_from_profiles(wl.WORKLOADS[HEADLINE].name, "prefill.hip"),

@@ -143,6 +143,46 @@ int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_s
                      int32_t G, int32_t head_dim, int32_t window, int32_t causal, float scale,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Varlen attention forward with the RoPE step fused into the tile loads
+ * ([kime-cpu plan.rs] `Ctx::step` Rope then Attention arms; [argus text.rs]
+ * `rope` then `block`).  The same result as kattn_rope_prologue at positions
+ * pos[r] = r - cu[s] followed by kattn_varlen_fwd, up to rounding order, but
+ * q and k are read-only: each q row is rotated as it is loaded and each k row
+ * as it is staged, so the separate in-place pass over q and k disappears.
+ *   q, k:       device float, UNROTATED (layout as in kattn_varlen_fwd).
+ *   cos, sin:   device float[table_len][32] (from kattn_rope_tables), required;
+ *               table_len >= max_seqlen.
+ * Every other argument as in kattn_varlen_fwd (same workspace size).
+ * Errors: as kattn_varlen_fwd, plus EINVAL for NULL tables and EBOUNDS for
+ * table_len < max_seqlen.
+ */
+int kattn_varlen_fwd_rope(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                          const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                          const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen, int32_t H,
+                          int32_t G, int32_t head_dim, int32_t window, int32_t causal, float scale,
+                          const float* cos, const float* sin, int32_t table_len, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Varlen attention forward with a binary16 output ([kime-cuda plan.rs] the
+ * attention variants that store a half output for a half tower; q, k and v
+ * stay FP32 and every step computes in FP32).  Each output element is the
+ * FP32 result rounded to the nearest binary16 (ties to even).
+ *   out:        device IEEE binary16 (T, H*64), row stride out_stride in
+ *               halves, a multiple of 8 (16 bytes); 16-byte aligned.
+ *   cos, sin:   both NULL when q and k are already rotated (as for
+ *               kattn_varlen_fwd), or the tables for fused rotation (as for
+ *               kattn_varlen_fwd_rope, table_len >= max_seqlen).
+ * Every other argument as in kattn_varlen_fwd (same workspace size).
+ */
+int kattn_varlen_fwd_f16(void* out, int64_t out_stride, const float* q, int64_t q_stride,
+                         const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                         const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen, int32_t H,
+                         int32_t G, int32_t head_dim, int32_t window, int32_t causal, float scale,
+                         const float* cos, const float* sin, int32_t table_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace kattn_decode needs for B sequences, H q heads and G kv
  * heads (0 for invalid sizes).  The size does not depend on the cache lengths. */
 size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G);

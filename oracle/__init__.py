@@ -56,9 +56,10 @@ def _load():
         lib.oracle_rope_apply.argtypes = [p, i64, p, i64, i32, i32, p, p, p, i32]
         lib.oracle_varlen_attention.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i32, i32, i32,
                                                 i32, i32, i32, f64, p, p, i32, p, i32, i32, i32]
+        lib.oracle_varlen_attention64.argtypes = lib.oracle_varlen_attention.argtypes
         lib.oracle_decode.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, f64, p, p, i32, i32]
         for f in (lib.oracle_rope_tables, lib.oracle_rope_apply, lib.oracle_varlen_attention,
-                  lib.oracle_decode):
+                  lib.oracle_varlen_attention64, lib.oracle_decode):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -110,8 +111,9 @@ def rope_apply(x, heads: int, pos, cos, sin):
 
 def varlen_attention(q, k, v, cu, H: int, G: int, window: int = -1, causal: bool = False,
                      scale: float = 0.125, tables=None, rows=None, mask_mode: int = 0,
-                     threads: int = 0):
-    """Attention output (T or len(rows), H*64) in f32, from f64 arithmetic.
+                     threads: int = 0, out_dtype=np.float32):
+    """Attention output (T or len(rows), H*64) from f64 arithmetic: rounded once to f32, or
+    left in f64 with ``out_dtype=np.float64`` (for outputs rounded to another precision).
 
     ``q``, ``k``, ``v`` are 2-D float32 arrays whose last axis may be a column
     slice of a packed qkv row (strides are passed through).  ``tables`` is the
@@ -125,10 +127,14 @@ def varlen_attention(q, k, v, cu, H: int, G: int, window: int = -1, causal: bool
     v, vs = _rows_view(v, G * HEAD_DIM)
     rows_a = None if rows is None else _i32(rows)
     n_out = T if rows_a is None else rows_a.shape[0]
-    out = np.empty((n_out, H * HEAD_DIM), np.float32)
+    wide = np.dtype(out_dtype) == np.float64
+    if not wide and np.dtype(out_dtype) != np.float32:
+        raise ValueError("out_dtype must be float32 or float64")
+    out = np.empty((n_out, H * HEAD_DIM), np.float64 if wide else np.float32)
     cos, sin = (None, None) if tables is None else (_f32(tables[0]), _f32(tables[1]))
     tl = 0 if cos is None else cos.shape[0]
-    rc = _load().oracle_varlen_attention(
+    fn = _load().oracle_varlen_attention64 if wide else _load().oracle_varlen_attention
+    rc = fn(
         _ptr(out), H * HEAD_DIM, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu), S, T, H, G,
         int(window), int(bool(causal)), float(scale), _ptr(cos), _ptr(sin), tl, _ptr(rows_a),
         0 if rows_a is None else rows_a.shape[0], int(mask_mode), int(threads))

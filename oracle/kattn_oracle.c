@@ -156,12 +156,13 @@ static int check_cu(const int32_t* cu, int32_t S, int32_t T) {
  *              skip the argus text.rs module docs argue is bit-identical).
  * threads <= 0: the OpenMP default.
  */
-int oracle_varlen_attention(float* out, int64_t out_stride, const float* q, int64_t q_stride,
-                            const float* k, int64_t k_stride, const float* v, int64_t v_stride,
-                            const int32_t* cu, int32_t S, int32_t T, int32_t H, int32_t G,
-                            int32_t window, int32_t causal, double scale, const float* cos_t,
-                            const float* sin_t, int32_t table_len, const int32_t* rows,
-                            int32_t nrows, int32_t mask_mode, int32_t threads) {
+static int varlen_attention(void* out, int out_f64, int64_t out_stride, const float* q,
+                            int64_t q_stride, const float* k, int64_t k_stride, const float* v,
+                            int64_t v_stride, const int32_t* cu, int32_t S, int32_t T, int32_t H,
+                            int32_t G, int32_t window, int32_t causal, double scale,
+                            const float* cos_t, const float* sin_t, int32_t table_len,
+                            const int32_t* rows, int32_t nrows, int32_t mask_mode,
+                            int32_t threads) {
     if (check_cu(cu, S, T) != 0) return -1;
     if (!out || !q || !k || !v || H < 1 || G < 1 || H % G != 0) return -1;
     if (q_stride < (int64_t)H * HD || k_stride < (int64_t)G * HD || v_stride < (int64_t)G * HD)
@@ -236,8 +237,13 @@ int oracle_varlen_attention(float* out, int64_t out_stride, const float* q, int6
                         const float* vj = v + (int64_t)(lo + j) * v_stride + (int64_t)g * HD;
                         for (int d = 0; d < HD; ++d) o[d] += p * (double)vj[d];
                     }
-                    float* orow = out + (int64_t)t * out_stride + (int64_t)h * HD;
-                    for (int d = 0; d < HD; ++d) orow[d] = (float)o[d];
+                    if (out_f64) {
+                        double* orow = (double*)out + (int64_t)t * out_stride + (int64_t)h * HD;
+                        for (int d = 0; d < HD; ++d) orow[d] = o[d];
+                    } else {
+                        float* orow = (float*)out + (int64_t)t * out_stride + (int64_t)h * HD;
+                        for (int d = 0; d < HD; ++d) orow[d] = (float)o[d];
+                    }
                 }
             }
         }
@@ -245,6 +251,32 @@ int oracle_varlen_attention(float* out, int64_t out_stride, const float* q, int6
         free(e);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_varlen_attention(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                            const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                            const int32_t* cu, int32_t S, int32_t T, int32_t H, int32_t G,
+                            int32_t window, int32_t causal, double scale, const float* cos_t,
+                            const float* sin_t, int32_t table_len, const int32_t* rows,
+                            int32_t nrows, int32_t mask_mode, int32_t threads) {
+    return varlen_attention(out, 0, out_stride, q, q_stride, k, k_stride, v, v_stride, cu, S, T,
+                            H, G, window, causal, scale, cos_t, sin_t, table_len, rows, nrows,
+                            mask_mode, threads);
+}
+
+/*
+ * The same, with the FP64 result left unrounded (for outputs of another
+ * precision, which are then rounded once from FP64).
+ */
+int oracle_varlen_attention64(double* out, int64_t out_stride, const float* q, int64_t q_stride,
+                              const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                              const int32_t* cu, int32_t S, int32_t T, int32_t H, int32_t G,
+                              int32_t window, int32_t causal, double scale, const float* cos_t,
+                              const float* sin_t, int32_t table_len, const int32_t* rows,
+                              int32_t nrows, int32_t mask_mode, int32_t threads) {
+    return varlen_attention(out, 1, out_stride, q, q_stride, k, k_stride, v, v_stride, cu, S, T,
+                            H, G, window, causal, scale, cos_t, sin_t, table_len, rows, nrows,
+                            mask_mode, threads);
 }
 
 /*

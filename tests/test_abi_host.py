@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     assert set(names) == set(kattn.EXPORTS)
     L = kattn.lib()
     for n in names:
@@ -104,6 +104,46 @@ def _fwd(**kw):
 def test_varlen_fwd_rejects_bad_arguments_on_the_host(kw, code):
     assert _fwd(**kw) == code
     assert kattn.lib().kattn_last_error()
+
+
+def _fwd_tab(fn, **kw):
+    a = dict(out=P(256), out_stride=256, q=P(256), q_stride=768, k=P(256), k_stride=768,
+             v=P(256), v_stride=768, cu=P(256), S=2, T=128, max_seqlen=91, H=4, G=4,
+             head_dim=64, window=-1, causal=0, scale=0.125, cos=P(512), sin=P(512),
+             table_len=91, workspace=P(4096), workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return getattr(kattn.lib(), fn)(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cos=None, sin=None), kattn.KATTN_EINVAL),
+    (dict(sin=None), kattn.KATTN_EINVAL),
+    (dict(table_len=90), kattn.KATTN_EBOUNDS),
+    (dict(cos=P(520)), kattn.KATTN_EUNSUPPORTED),
+    (dict(head_dim=128), kattn.KATTN_EUNSUPPORTED),
+    (dict(workspace_bytes=16), kattn.KATTN_EBOUNDS),
+])
+def test_varlen_fwd_rope_rejects_bad_arguments_on_the_host(kw, code):
+    assert _fwd_tab("kattn_varlen_fwd_rope", **kw) == code
+    assert kattn.lib().kattn_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out_stride=260), kattn.KATTN_EUNSUPPORTED),   # binary16 rows: multiples of 8 halves
+    (dict(out_stride=255), kattn.KATTN_EBOUNDS),
+    (dict(sin=None), kattn.KATTN_EINVAL),
+    (dict(table_len=90), kattn.KATTN_EBOUNDS),
+    (dict(out=P(264)), kattn.KATTN_EUNSUPPORTED),
+])
+def test_varlen_fwd_f16_rejects_bad_arguments_on_the_host(kw, code):
+    assert _fwd_tab("kattn_varlen_fwd_f16", **kw) == code
+    assert kattn.lib().kattn_last_error()
+
+
+def test_varlen_fwd_variants_empty_batch_queues_nothing():
+    assert _fwd_tab("kattn_varlen_fwd_rope", T=0, max_seqlen=0, table_len=0) == kattn.KATTN_OK
+    assert _fwd_tab("kattn_varlen_fwd_f16", S=0, T=0, max_seqlen=0, cos=None, sin=None,
+                    table_len=0) == kattn.KATTN_OK
 
 
 def test_varlen_fwd_empty_batch_queues_nothing():

@@ -289,3 +289,96 @@ def test_decode_batch_beyond_one_launch():
     case = _decode_case(lens, 4, 2, 64, seed=6)
     case.used[7] = 1
     _check_decode(case, rotate=True)
+
+
+# ----------------------------------------------------------------------------- fused RoPE (read-only q/k)
+
+def gpu_prefill_fused(case, pad_rows=0, sentinel=None):
+    run = PrefillRun(case, out_pad_rows=pad_rows)
+    if sentinel is not None:
+        run.out_full.fill_(sentinel)
+    run.step_fused()
+    torch.cuda.synchronize()
+    return run
+
+
+@pytest.mark.parametrize("lengths,H,G,window,causal", SMALL_CASES)
+def test_fused_rope_small_cases(lengths, H, G, window, causal):
+    case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
+                           theta=10000.0, seed=200 + len(lengths) + H + window)
+    run = gpu_prefill_fused(case, pad_rows=5, sentinel=float("nan"))
+    got = run.out_full.cpu().numpy()
+    ref = oracle_prefill(case)
+    assert max_err(got[:case.T], ref) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))
+    # q and k are read-only in the fused path
+    assert np.array_equal(run.q.cpu().numpy(), case.q)
+    assert np.array_equal(run.k.cpu().numpy(), case.k)
+
+
+@pytest.mark.parametrize("key", ["0", "1", "3a"])
+def test_fused_rope_workload_full_parity(key):
+    case = wl.build(key)
+    got = gpu_prefill_fused(case).out.cpu().numpy()
+    assert max_err(got, oracle_prefill(case)) <= ATOL
+
+
+@pytest.mark.parametrize("key", ["2", "3b"])
+def test_fused_rope_workload_sampled_parity(key):
+    case = wl.build(key)
+    got = gpu_prefill_fused(case).out.cpu().numpy()
+    rows = _sample_rows(case, 24, 9)
+    assert max_err(got[rows], oracle_prefill(case, rows=rows)) <= ATOL
+    assert np.all(np.isfinite(got))
+
+
+def test_fused_rope_matches_prologue_then_attention():
+    case = wl.make_prefill([300, 5, 129], 9, 3, packed=False, causal=True, theta=100000.0, seed=21)
+    fused = gpu_prefill_fused(case).out.cpu().numpy()
+    two_pass = gpu_prefill(case).out.cpu().numpy()
+    assert max_err(fused, two_pass) <= ATOL
+
+
+# ----------------------------------------------------------------------------- binary16 output
+
+def _f16_bound(ref64, got16):
+    """Per element: half a binary16 ulp (at the larger of the two magnitudes) plus the FP32 bar."""
+    a = np.maximum(np.abs(ref64), np.abs(got16.astype(np.float64))).astype(np.float16)
+    return 0.5 * np.spacing(a).astype(np.float64) + ATOL
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("lengths,H,G,window,causal", [SMALL_CASES[2], SMALL_CASES[8],
+                                                        SMALL_CASES[9], SMALL_CASES[16]])
+def test_f16_output_small_cases(fused, lengths, H, G, window, causal):
+    case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
+                           theta=10000.0, seed=300 + len(lengths) + H)
+    run = PrefillRun(case)
+    out16 = torch.full((case.T + 3, H * D), float("nan"), dtype=torch.float16, device="cuda")
+    if not fused:
+        run.rope()
+    run.attention_f16(out16[:case.T], fused=fused)
+    torch.cuda.synchronize()
+    got = out16.cpu().numpy()
+    tables = oracle.rope_tables(case.theta, max(case.max_seqlen, 1))
+    ref64 = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, window, causal,
+                                    tables=tables, threads=16, out_dtype=np.float64)
+    err = np.abs(got[:case.T].astype(np.float64) - ref64)
+    assert np.all(err <= _f16_bound(ref64, got[:case.T]))
+    assert np.all(np.isnan(got[case.T:]))
+
+
+def test_f16_output_headline_workload():
+    case = wl.build("1")
+    run = PrefillRun(case)
+    out16 = torch.empty((case.T, case.H * D), dtype=torch.float16, device="cuda")
+    run.attention_f16(out16, fused=True)
+    torch.cuda.synchronize()
+    got = out16.cpu().numpy()
+    rows = _sample_rows(case, 64, 11)
+    tables = oracle.rope_tables(case.theta, case.max_seqlen)
+    ref64 = oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
+                                    case.causal, tables=tables, rows=rows, threads=16,
+                                    out_dtype=np.float64)
+    err = np.abs(got[rows].astype(np.float64) - ref64)
+    assert np.all(err <= _f16_bound(ref64, got[rows]))

@@ -415,3 +415,33 @@ def test_oracle_rejects_bad_offsets():
         oracle.varlen_attention(q, q, q, np.array([1, 4], np.int32), 1, 1)
     with pytest.raises(ValueError):
         oracle.varlen_attention(q, q, q, np.array([0, 4], np.int32), 3, 2)
+
+
+# ----------------------------------------------------------------------------- wide output
+
+def test_fp64_output_rounds_to_the_fp32_output_bit_for_bit():
+    # the FP64-output entry is the same arithmetic with the final rounding left out
+    rng = np.random.default_rng(31)
+    cu = np.array([0, 5, 40, 41], np.int32)
+    T, H, G = 41, 4, 2
+    q = rng.standard_normal((T, H * 64), dtype=np.float32)
+    k = rng.standard_normal((T, G * 64), dtype=np.float32)
+    v = rng.standard_normal((T, G * 64), dtype=np.float32)
+    tables = oracle.rope_tables(10000.0, 40)
+    for window, causal in [(-1, False), (8, True)]:
+        a = oracle.varlen_attention(q, k, v, cu, H, G, window, causal, tables=tables)
+        b = oracle.varlen_attention(q, k, v, cu, H, G, window, causal, tables=tables,
+                                    out_dtype=np.float64)
+        assert b.dtype == np.float64
+        assert np.array_equal(b.astype(np.float32), a)
+
+
+def test_binary16_rounding_step_is_round_to_nearest_even():
+    # the FP16-output comparison rounds the oracle's FP64 result once with numpy; pin that
+    # step on values whose binary16 encodings follow from the format's definition
+    cases = {1.0: 0x3C00, 1.0 / 3.0: 0x3555, 2049.0: 0x6800, 2051.0: 0x6802,
+             1.0 + 2.0 ** -11: 0x3C00, 1.0 + 3 * 2.0 ** -11: 0x3C02, 65504.0: 0x7BFF,
+             65520.0: 0x7C00, 2.0 ** -24: 0x0001, 2.0 ** -25: 0x0000, -0.5: 0xB800}
+    with np.errstate(over="ignore"):  # 65520 rounds up to infinity, as the format says
+        for x, bits in cases.items():
+            assert int(np.float64(x).astype(np.float16).view(np.uint16)) == bits, x

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------------------------
 struct FwdParams {
-    float* out;
+    void* out;  // float, or binary16 for the half-output variant
     const float* q;
     const float* k;
     const float* v;
@@ -209,15 +209,28 @@ struct FwdParams {
     const int2* tiles;
     const int32_t* count;
     int64_t out_stride, q_stride, k_stride, v_stride;
+    const float* cos_t;  // RoPE tables [table_len][32] for the fused-rotation variant
+    const float* sin_t;
+    int table_len;
     int T, H, R, nunits, hw, causal;
     float scale;
 };
+
+// Value held by lane l ^ 8 (DPP row_ror:8 inside each 16-lane row): the lane that holds the
+// other half of a rotation pair when 16 lanes cover one 64-float row, 4 floats each.
+__device__ inline float ror8(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
 
 // TBN: keys per K/V tile.  Global launches use 64-key tiles (two 32-key score blocks per MFMA
 // round, fewer barriers per flop).  Banded launches (a window or a causal limit) use 32-key
 // tiles: a wave's band is covered with less waste, and half the score and staging registers
 // leave room for a third wave per SIMD.
-template <int HPW, int QW, int TBN>
+// ROPE: q and k arrive unrotated; q is rotated as it is loaded and every K row as it is
+// staged in LDS, at its position inside the sequence (the RoPE step of kime-cpu plan.rs
+// `Ctx::step` and argus text.rs `rope`, moved into the tile loads).
+// F16: the output is written as IEEE binary16 (round to nearest even) instead of FP32.
+template <int HPW, int QW, int TBN, bool ROPE, bool F16>
 __global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(TBN == 32 ? 3 : 2)))
 void fwd_kernel(FwdParams p) {
     static_assert(TBN == 32 || TBN == 64, "tiles hold one or two 32-key score blocks");
@@ -245,24 +258,6 @@ void fwd_kernel(FwdParams p) {
     const bool wave_live = qa < n;
     const int qlast_w = min(qa + 31, n - 1);
 
-    // Q slice: dims 32hh .. 32hh+31 of query qi, times scale.
-    float qreg[32];
-    if (qi < n) {
-        const float4* src = reinterpret_cast<const float4*>(
-            p.q + static_cast<int64_t>(lo + qi) * p.q_stride + head * kHeadDim + hh * 32);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float4 t = src[m];
-            qreg[4 * m + 0] = t.x * p.scale;
-            qreg[4 * m + 1] = t.y * p.scale;
-            qreg[4 * m + 2] = t.z * p.scale;
-            qreg[4 * m + 3] = t.w * p.scale;
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
-    }
-
     f32x16 O0, O1;  // O^T accumulators: rows i -> dims 2i (O0) and 2i+1 (O1), column = query j
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -288,6 +283,12 @@ void fwd_kernel(FwdParams p) {
     const int lcol = threadIdx.x & 15;
     constexpr int rstep = NT / 16;
     float4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
+    // With ROPE each K row also brings one float4 of its table row: the lanes holding dims
+    // 0..31 fetch cos, the lanes holding dims 32..63 fetch sin of the same pairs, and the two
+    // swap them (ror8) when the row is rotated at staging time.
+    float4 pt0, pt1, pt2, pt3;
+    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+#define KATTN_TAB(R) (reinterpret_cast<const float4*>(tab + min(R, static_cast<int64_t>(p.table_len) - 1) * 32)[0])
 #define KATTN_FETCH(K0)                                                                         \
     {                                                                                           \
         const int64_t r0 = min((K0) + lrow, n - 1), r1 = min((K0) + lrow + rstep, n - 1);       \
@@ -295,6 +296,10 @@ void fwd_kernel(FwdParams p) {
         pk1 = reinterpret_cast<const float4*>(kbase + r1 * p.k_stride)[lcol];                  \
         pv0 = reinterpret_cast<const float4*>(vbase + r0 * p.v_stride)[lcol];                  \
         pv1 = reinterpret_cast<const float4*>(vbase + r1 * p.v_stride)[lcol];                  \
+        if constexpr (ROPE) {                                                                   \
+            pt0 = KATTN_TAB(r0);                                                                \
+            pt1 = KATTN_TAB(r1);                                                                \
+        }                                                                                       \
         if constexpr (TWO) {                                                                    \
             const int64_t r2 = min((K0) + lrow + 2 * rstep, n - 1);                             \
             const int64_t r3 = min((K0) + lrow + 3 * rstep, n - 1);                             \
@@ -302,10 +307,34 @@ void fwd_kernel(FwdParams p) {
             pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];              \
             pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];              \
             pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];              \
+            if constexpr (ROPE) {                                                               \
+                pt2 = KATTN_TAB(r2);                                                            \
+                pt3 = KATTN_TAB(r3);                                                            \
+            }                                                                                   \
+        }                                                                                       \
+    }
+    // rotate a staged K piece: x[i] c - x[i+32] s in the low lanes, x[i+32] c + x[i] s in the
+    // high lanes (the other half of each pair and the other table come from lane ^ 8)
+#define KATTN_ROT(X, TT)                                                                        \
+    if constexpr (ROPE) {                                                                       \
+        const float4 y = make_float4(ror8(X.x), ror8(X.y), ror8(X.z), ror8(X.w));               \
+        const float4 u = make_float4(ror8(TT.x), ror8(TT.y), ror8(TT.z), ror8(TT.w));           \
+        if (lcol < 8) {                                                                         \
+            X = make_float4(X.x * TT.x - y.x * u.x, X.y * TT.y - y.y * u.y,                     \
+                            X.z * TT.z - y.z * u.z, X.w * TT.w - y.w * u.w);                    \
+        } else {                                                                                \
+            X = make_float4(X.x * u.x + y.x * TT.x, X.y * u.y + y.y * TT.y,                     \
+                            X.z * u.z + y.z * TT.z, X.w * u.w + y.w * TT.w);                    \
         }                                                                                       \
     }
 #define KATTN_STASH()                                                                           \
     {                                                                                           \
+        KATTN_ROT(pk0, pt0)                                                                     \
+        KATTN_ROT(pk1, pt1)                                                                     \
+        if constexpr (TWO) {                                                                    \
+            KATTN_ROT(pk2, pt2)                                                                 \
+            KATTN_ROT(pk3, pt3)                                                                 \
+        }                                                                                       \
         float* kd = &Ks[lrow * LDS_STRIDE + 4 * lcol];                                          \
         float* vd = &Vs[lrow * LDS_STRIDE + 4 * lcol];                                          \
         *reinterpret_cast<float4*>(kd) = pk0;                                                   \
@@ -319,7 +348,57 @@ void fwd_kernel(FwdParams p) {
             *reinterpret_cast<float4*>(vd + 3 * rstep * LDS_STRIDE) = pv3;                      \
         }                                                                                       \
     }
+    // the first tile's loads go out before the Q loads, so the two latencies overlap
     KATTN_FETCH(kbeg)
+
+    // Q slice: dims 32hh .. 32hh+31 of query qi, times scale.
+    float qreg[32];
+    if (qi < n) {
+        const float* qrow = p.q + static_cast<int64_t>(lo + qi) * p.q_stride + head * kHeadDim;
+        const float4* src = reinterpret_cast<const float4*>(qrow + hh * 32);
+        if constexpr (ROPE) {
+            // pairs (x[i], x[i+32]) at position qi: the low lane half loads dims 0..31 and the
+            // cos row, the high half dims 32..63 and the sin row; a permlane32 swap then gives
+            // every lane both members of each pair and both tables (low value first).
+            const int64_t prow = min(qi, p.table_len - 1);
+            const float4* tq = reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
+            float4 xa[8], ta[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                xa[m] = src[m];
+                ta[m] = tq[m];
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+                const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
+                                                                     __float_as_uint(xs[c]), false, false);
+                    const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
+                                                                     __float_as_uint(ts[c]), false, false);
+                    const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
+                    const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
+                    const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
+                    qreg[4 * m + c] = r * p.scale;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 t = src[m];
+                qreg[4 * m + 0] = t.x * p.scale;
+                qreg[4 * m + 1] = t.y * p.scale;
+                qreg[4 * m + 2] = t.z * p.scale;
+                qreg[4 * m + 3] = t.w * p.scale;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
+    }
+
     KATTN_STASH()
     __syncthreads();
     for (int kt = kbeg; kt < kend; kt += TBN) {
@@ -436,11 +515,13 @@ void fwd_kernel(FwdParams p) {
     }
 #undef KATTN_FETCH
 #undef KATTN_STASH
+#undef KATTN_ROT
+#undef KATTN_TAB
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (qi < n) {
         const float inv = 1.0f / l_tot;
-        float* dst = p.out + static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim;
+        const int64_t at = static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim;
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
             const int i0 = 8 * grp + 4 * hh;  // result rows i0..i0+3 -> dims 2*i0 .. 2*i0+7
@@ -454,8 +535,24 @@ void fwd_kernel(FwdParams p) {
             b.y = O1[r0 + 2] * inv;
             b.z = O0[r0 + 3] * inv;
             b.w = O1[r0 + 3] * inv;
-            *reinterpret_cast<float4*>(dst + 2 * i0) = a;
-            *reinterpret_cast<float4*>(dst + 2 * i0 + 4) = b;
+            if constexpr (F16) {
+                // dims 2*i0 .. 2*i0+7 as eight halves: one 16-byte store
+                typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+                h8 hv;
+                hv[0] = static_cast<_Float16>(a.x);
+                hv[1] = static_cast<_Float16>(a.y);
+                hv[2] = static_cast<_Float16>(a.z);
+                hv[3] = static_cast<_Float16>(a.w);
+                hv[4] = static_cast<_Float16>(b.x);
+                hv[5] = static_cast<_Float16>(b.y);
+                hv[6] = static_cast<_Float16>(b.z);
+                hv[7] = static_cast<_Float16>(b.w);
+                *reinterpret_cast<h8*>(static_cast<_Float16*>(p.out) + at + 2 * i0) = hv;
+            } else {
+                float* dst = static_cast<float*>(p.out) + at;
+                *reinterpret_cast<float4*>(dst + 2 * i0) = a;
+                *reinterpret_cast<float4*>(dst + 2 * i0 + 4) = b;
+            }
         }
     }
 }
@@ -474,14 +571,21 @@ Shape pick_shape(int R) {
     }
 }
 
-template <int HPW, int QW>
+template <int HPW, int QW, bool ROPE, bool F16>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
     if (p.causal || p.hw >= 0)
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32, ROPE, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64, ROPE, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
+}
+
+template <bool ROPE, bool F16>
+void launch_shape(const Shape& sh, const FwdParams& p, int64_t grid, hipStream_t stream) {
+    if (sh.hpw == 1) launch_fwd<1, 4, ROPE, F16>(p, grid, stream);
+    else if (sh.hpw == 2) launch_fwd<2, 2, ROPE, F16>(p, grid, stream);
+    else launch_fwd<4, 1, ROPE, F16>(p, grid, stream);
 }
 
 }  // namespace
@@ -495,13 +599,16 @@ extern "C" size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T) {
     return kHeader + prefix_bytes(S) + static_cast<size_t>(tile_capacity(S, T, 32)) * sizeof(int2);
 }
 
-extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_stride,
-                                const float* k, int64_t k_stride, const float* v, int64_t v_stride,
-                                const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen,
-                                int32_t H, int32_t G, int32_t head_dim, int32_t window,
-                                int32_t causal, float scale, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "kattn_varlen_fwd";
+namespace {
+
+// The shared body of the forward entry points: checks, planning launch, tile launch.
+// cos/sin non-NULL selects the fused-rotation kernels; out_f16 the binary16 output.
+int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, int64_t q_stride,
+               const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+               const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen, int32_t H, int32_t G,
+               int32_t head_dim, int32_t window, int32_t causal, float scale, const float* cos,
+               const float* sin, int32_t table_len, bool out_f16, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
     if (head_dim != kHeadDim)
         return fail(KATTN_EUNSUPPORTED, "%s: head_dim %d, only 64 is supported", fn, head_dim);
     if (S < 0 || T < 0 || H < 1 || G < 1)
@@ -513,13 +620,20 @@ extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, 
         return fail(KATTN_EINVAL, "%s: scale must be finite and > 0", fn);
     if (max_seqlen < 0 || max_seqlen > T)
         return fail(KATTN_EBOUNDS, "%s: max_seqlen %d outside [0, T=%d]", fn, max_seqlen, T);
+    const bool rope = cos != nullptr || sin != nullptr;
+    if (rope && (cos == nullptr || sin == nullptr))
+        return fail(KATTN_EINVAL, "%s: cos and sin must both be given or both be NULL", fn);
+    if (rope && table_len < max_seqlen)
+        return fail(KATTN_EBOUNDS, "%s: table_len %d < max_seqlen %d", fn, table_len, max_seqlen);
     if (T == 0 || S == 0) return ok();
     if (!out || !q || !k || !v || !cu || !workspace) return fail(KATTN_EINVAL, "%s: null pointer", fn);
     if (out_stride < static_cast<int64_t>(H) * kHeadDim || q_stride < static_cast<int64_t>(H) * kHeadDim ||
         k_stride < static_cast<int64_t>(G) * kHeadDim || v_stride < static_cast<int64_t>(G) * kHeadDim)
         return fail(KATTN_EBOUNDS, "%s: a row stride is narrower than its heads", fn);
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || (out_stride & 3) ||
-        (q_stride & 3) || (k_stride & 3) || (v_stride & 3))
+    // 16-byte accesses: float strides in multiples of 4, binary16 output strides of 8
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        (out_stride & (out_f16 ? 7 : 3)) || (q_stride & 3) || (k_stride & 3) || (v_stride & 3) ||
+        (rope && (!aligned16(cos) || !aligned16(sin))))
         return fail(KATTN_EUNSUPPORTED, "%s: pointers and strides must be multiples of 16 bytes", fn);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
@@ -571,6 +685,9 @@ extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, 
     p.q_stride = q_stride;
     p.k_stride = k_stride;
     p.v_stride = v_stride;
+    p.cos_t = cos;
+    p.sin_t = sin;
+    p.table_len = rope ? table_len : 0;
     p.T = T;
     p.H = H;
     p.R = R;
@@ -578,8 +695,49 @@ extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, 
     p.hw = hw;
     p.causal = causal;
     p.scale = scale;
-    if (sh.hpw == 1) launch_fwd<1, 4>(p, grid, stream);
-    else if (sh.hpw == 2) launch_fwd<2, 2>(p, grid, stream);
-    else launch_fwd<4, 1>(p, grid, stream);
+    if (rope && out_f16) launch_shape<true, true>(sh, p, grid, stream);
+    else if (rope) launch_shape<true, false>(sh, p, grid, stream);
+    else if (out_f16) launch_shape<false, true>(sh, p, grid, stream);
+    else launch_shape<false, false>(sh, p, grid, stream);
     return check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" int kattn_varlen_fwd(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                                const float* k, int64_t k_stride, const float* v, int64_t v_stride,
+                                const int32_t* cu, int32_t S, int32_t T, int32_t max_seqlen,
+                                int32_t H, int32_t G, int32_t head_dim, int32_t window,
+                                int32_t causal, float scale, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    return varlen_fwd("kattn_varlen_fwd", out, out_stride, q, q_stride, k, k_stride, v, v_stride,
+                      cu, S, T, max_seqlen, H, G, head_dim, window, causal, scale, nullptr,
+                      nullptr, 0, false, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kattn_varlen_fwd_rope(float* out, int64_t out_stride, const float* q,
+                                     int64_t q_stride, const float* k, int64_t k_stride,
+                                     const float* v, int64_t v_stride, const int32_t* cu,
+                                     int32_t S, int32_t T, int32_t max_seqlen, int32_t H, int32_t G,
+                                     int32_t head_dim, int32_t window, int32_t causal, float scale,
+                                     const float* cos, const float* sin, int32_t table_len,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kattn_varlen_fwd_rope";
+    if (cos == nullptr || sin == nullptr)
+        return fail(KATTN_EINVAL, "%s: cos and sin are required", fn);
+    return varlen_fwd(fn, out, out_stride, q, q_stride, k, k_stride, v, v_stride, cu, S, T,
+                      max_seqlen, H, G, head_dim, window, causal, scale, cos, sin, table_len,
+                      false, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kattn_varlen_fwd_f16(void* out, int64_t out_stride, const float* q,
+                                    int64_t q_stride, const float* k, int64_t k_stride,
+                                    const float* v, int64_t v_stride, const int32_t* cu,
+                                    int32_t S, int32_t T, int32_t max_seqlen, int32_t H, int32_t G,
+                                    int32_t head_dim, int32_t window, int32_t causal, float scale,
+                                    const float* cos, const float* sin, int32_t table_len,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return varlen_fwd("kattn_varlen_fwd_f16", out, out_stride, q, q_stride, k, k_stride, v,
+                      v_stride, cu, S, T, max_seqlen, H, G, head_dim, window, causal, scale, cos,
+                      sin, table_len, true, workspace, workspace_bytes, stream);
 }

@@ -23,8 +23,8 @@ KATTN_EBOUNDS = -3
 KATTN_EDEVICE = -4
 
 EXPORTS = ("kattn_last_error", "kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
-           "kattn_varlen_fwd_workspace", "kattn_varlen_fwd", "kattn_decode_workspace",
-           "kattn_decode")
+           "kattn_varlen_fwd_workspace", "kattn_varlen_fwd", "kattn_varlen_fwd_rope",
+           "kattn_varlen_fwd_f16", "kattn_decode_workspace", "kattn_decode")
 
 
 class KattnError(RuntimeError):
@@ -55,12 +55,17 @@ def lib():
         L.kattn_varlen_fwd_workspace.restype = sz
         L.kattn_varlen_fwd.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i32, i32, i32, i32, i32,
                                        i32, i32, i32, f32, p, sz, p]
+        fwd_tab = [p, i64, p, i64, p, i64, p, i64, p, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                   p, p, i32, p, sz, p]
+        L.kattn_varlen_fwd_rope.argtypes = fwd_tab
+        L.kattn_varlen_fwd_f16.argtypes = fwd_tab
         L.kattn_decode_workspace.argtypes = [i32, i32, i32]
         L.kattn_decode_workspace.restype = sz
         L.kattn_decode.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, f32, p, p,
                                    i32, p, sz, p]
         for name in ("kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
-                     "kattn_varlen_fwd", "kattn_decode"):
+                     "kattn_varlen_fwd", "kattn_varlen_fwd_rope", "kattn_varlen_fwd_f16",
+                     "kattn_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,6 +147,31 @@ def kattn_varlen_fwd(out, q, k, v, cu, S: int, T: int, max_seqlen: int, H: int, 
                                   _dev(v), _stride(v), _dev(cu), S, T, max_seqlen, H, G, HEAD_DIM,
                                   int(window), int(bool(causal)), float(scale), _dev(workspace),
                                   ws_bytes, _stream(stream)))
+
+
+def kattn_varlen_fwd_rope(out, q, k, v, cu, S: int, T: int, max_seqlen: int, H: int, G: int,
+                          cos, sin, *, window: int = -1, causal: bool = False,
+                          scale: float = 0.125, workspace=None, stream=None):
+    """Varlen attention over UNROTATED q/k, rotated inside the tile loads (q, k read-only)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kattn_varlen_fwd_rope(_dev(out), _stride(out), _dev(q), _stride(q), _dev(k),
+                                       _stride(k), _dev(v), _stride(v), _dev(cu), S, T, max_seqlen,
+                                       H, G, HEAD_DIM, int(window), int(bool(causal)),
+                                       float(scale), _dev(cos), _dev(sin), int(cos.shape[0]),
+                                       _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def kattn_varlen_fwd_f16(out, q, k, v, cu, S: int, T: int, max_seqlen: int, H: int, G: int, *,
+                         cos=None, sin=None, window: int = -1, causal: bool = False,
+                         scale: float = 0.125, workspace=None, stream=None):
+    """Varlen attention with a float16 ``out`` tensor; ``cos``/``sin`` select fused rotation."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    table_len = 0 if cos is None else int(cos.shape[0])
+    _check(lib().kattn_varlen_fwd_f16(_dev(out), _stride(out), _dev(q), _stride(q), _dev(k),
+                                      _stride(k), _dev(v), _stride(v), _dev(cu), S, T, max_seqlen,
+                                      H, G, HEAD_DIM, int(window), int(bool(causal)),
+                                      float(scale), _dev(cos), _dev(sin), table_len,
+                                      _dev(workspace), ws_bytes, _stream(stream)))
 
 
 def kattn_decode(out, q, k_new, v_new, k_cache, v_cache, cap: int, used, max_used: int, B: int,

@@ -3,7 +3,8 @@
 This is call sequencing only -- every step of the path runs in libkattn.so:
 
   prefill:  kattn_build_index (host) -> copy cu/pos to HBM -> kattn_rope_prologue
-            (in place on q and k) -> kattn_varlen_fwd
+            (in place on q and k) -> kattn_varlen_fwd; or, fused, kattn_varlen_fwd_rope
+            (q and k read-only, rotated inside the tile loads)
   decode:   kattn_decode (rotate + append + split-K + combine)
 
 Inputs are copied to HBM once when a run is created; ``step()`` then touches
@@ -74,6 +75,26 @@ class PrefillRun:
         kattn.kattn_varlen_fwd(self.out, self.q, self.k, self.v, self.cu, c.S, c.T,
                                self.max_seqlen, c.H, c.G, window=c.window, causal=c.causal,
                                scale=0.125, workspace=self.workspace)
+
+    def attention_rope(self, out=None):
+        """Attention with the rotation fused into the tile loads (q, k must be unrotated)."""
+        c = self.case
+        kattn.kattn_varlen_fwd_rope(self.out if out is None else out, self.q, self.k, self.v,
+                                    self.cu, c.S, c.T, self.max_seqlen, c.H, c.G, self.cos,
+                                    self.sin, window=c.window, causal=c.causal, scale=0.125,
+                                    workspace=self.workspace)
+
+    def attention_f16(self, out16, fused: bool):
+        """Attention with a float16 output; ``fused`` rotates unrotated q/k in the tile loads."""
+        c = self.case
+        kattn.kattn_varlen_fwd_f16(out16, self.q, self.k, self.v, self.cu, c.S, c.T,
+                                   self.max_seqlen, c.H, c.G, cos=self.cos if fused else None,
+                                   sin=self.sin if fused else None, window=c.window,
+                                   causal=c.causal, scale=0.125, workspace=self.workspace)
+
+    def step_fused(self):
+        """One pass of the prefill path with RoPE fused into attention (q, k left as they are)."""
+        self.attention_rope()
 
     def step(self):
         """One pass of the prefill path: RoPE prologue then attention (on rotated q/k).
