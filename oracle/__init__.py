@@ -58,8 +58,10 @@ def _load():
                                                 i32, i32, i32, f64, p, p, i32, p, i32, i32, i32]
         lib.oracle_varlen_attention64.argtypes = lib.oracle_varlen_attention.argtypes
         lib.oracle_decode.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, f64, p, p, i32, i32]
+        lib.oracle_prefill_cached.argtypes = [p, i64, p, i64, p, i64, p, i64, p, p, i32, i32, p, p,
+                                              i32, i32, i32, f64, p, p, i32, i32]
         for f in (lib.oracle_rope_tables, lib.oracle_rope_apply, lib.oracle_varlen_attention,
-                  lib.oracle_varlen_attention64, lib.oracle_decode):
+                  lib.oracle_varlen_attention64, lib.oracle_decode, lib.oracle_prefill_cached):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -161,4 +163,31 @@ def decode(q_new, k_new, v_new, k_cache, v_cache, used, H: int, G: int, scale: f
                                _ptr(sin), tl, int(threads))
     if rc != 0:
         raise ValueError("oracle_decode: bad arguments")
+    return out, kc, vc
+
+
+def prefill_cached(q, k_new, v_new, cu, offset, k_cache, v_cache, H: int, G: int,
+                   scale: float = 0.125, tables=None, threads: int = 0):
+    """Chunked prefill continuing from a KV cache (argus text.rs `KvAppend` + `CausalSoftmax`
+    with an offset).  Returns (out [T, H*64], k_cache', v_cache'): the caches are copies with
+    the chunk's rotated keys and values appended at rows offset[b] ..; the arrays passed in
+    are left as they were."""
+    cu, offset = _i32(cu), _i32(offset)
+    B = cu.shape[0] - 1
+    T = int(cu[-1]) if B >= 0 else 0
+    q, qs = _rows_view(q, H * HEAD_DIM)
+    k_new, ks = _rows_view(k_new, G * HEAD_DIM)
+    v_new, vs = _rows_view(v_new, G * HEAD_DIM)
+    kc = np.array(k_cache, dtype=np.float32, copy=True, order="C")
+    vc = np.array(v_cache, dtype=np.float32, copy=True, order="C")
+    cap = kc.shape[2]
+    out = np.empty((T, H * HEAD_DIM), np.float32)
+    cos, sin = (None, None) if tables is None else (_f32(tables[0]), _f32(tables[1]))
+    tl = 0 if cos is None else cos.shape[0]
+    rc = _load().oracle_prefill_cached(_ptr(out), H * HEAD_DIM, _ptr(q), qs, _ptr(k_new), ks,
+                                       _ptr(v_new), vs, _ptr(cu), _ptr(offset), B, T, _ptr(kc),
+                                       _ptr(vc), cap, H, G, float(scale), _ptr(cos), _ptr(sin), tl,
+                                       int(threads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_cached: bad arguments")
     return out, kc, vc

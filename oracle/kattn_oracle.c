@@ -373,3 +373,114 @@ int oracle_decode(float* out, const float* q_new, const float* k_new, const floa
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Chunked prefill that continues from a KV cache (ffai-argus text.rs:
+ * `KvAppend` at the cache's fill point, then `CausalSoftmax` with q_len > 1
+ * and an offset, whose causal limit for query i is key offset + i).
+ *
+ * Sequence b of the batch brings n_b = cu[b+1] - cu[b] new rows (packed rows
+ * cu[b] .. cu[b+1]-1 of q, k_new, v_new) and already holds off_b = offset[b]
+ * rows in its caches [B][G][cap][64].  Reading taken: the new rows sit at
+ * positions off_b + i (RoPE and cache row), which is where the page's
+ * append puts them.  For each b:
+ *   1. k_new row i is rotated at off_b + i (f64, rounded to f32) and written
+ *      with v_new row i into cache row off_b + i of every kv head;
+ *   2. q row i is rotated at off_b + i and kept in f64;
+ *   3. it is scored against the stored f32 cache rows 0 .. off_b + i (rows
+ *      past the causal limit are masked out, which is the same as -inf);
+ *   4. two-pass softmax and P.V in f64, one rounding to f32, into out row
+ *      cu[b] + i.
+ * With n_b = 1 this is exactly one decode step with L = off_b + 1, and the
+ * arithmetic is done in the same order as oracle_decode.
+ * Requires 0 <= off_b and off_b + n_b <= cap (and <= table_len when rotating).
+ * The caches passed in are modified (the caller hands the oracle copies).
+ */
+int oracle_prefill_cached(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                          const float* k_new, int64_t k_stride, const float* v_new,
+                          int64_t v_stride, const int32_t* cu, const int32_t* offset, int32_t B,
+                          int32_t T, float* k_cache, float* v_cache, int32_t cap, int32_t H,
+                          int32_t G, double scale, const float* cos_t, const float* sin_t,
+                          int32_t table_len, int32_t threads) {
+    if (check_cu(cu, B, T) != 0) return -1;
+    if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !offset) return -1;
+    if (H < 1 || G < 1 || H % G != 0 || cap < 1) return -1;
+    if (q_stride < (int64_t)H * HD || k_stride < (int64_t)G * HD || v_stride < (int64_t)G * HD ||
+        out_stride < (int64_t)H * HD)
+        return -1;
+    if ((cos_t == NULL) != (sin_t == NULL)) return -1;
+    int32_t max_ctx = 1;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t n = cu[b + 1] - cu[b];
+        if (offset[b] < 0 || (int64_t)offset[b] + n > cap) return -1;
+        if (cos_t && (int64_t)offset[b] + n > table_len) return -1;
+        if (offset[b] + n > max_ctx) max_ctx = offset[b] + n;
+    }
+    const int32_t R = H / G;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+    /* step 1: append the chunk */
+    for (int32_t b = 0; b < B; ++b) {
+        for (int32_t i = 0; i < cu[b + 1] - cu[b]; ++i) {
+            int32_t r = cu[b] + i, p = offset[b] + i;
+            for (int32_t g = 0; g < G; ++g) {
+                double kr[HD];
+                rope_head(k_new + (int64_t)r * k_stride + (int64_t)g * HD, cos_t, sin_t, p, kr);
+                float* krow = k_cache + (((int64_t)b * G + g) * cap + p) * HD;
+                float* vrow = v_cache + (((int64_t)b * G + g) * cap + p) * HD;
+                const float* vn = v_new + (int64_t)r * v_stride + (int64_t)g * HD;
+                for (int d = 0; d < HD; ++d) {
+                    krow[d] = (float)kr[d];
+                    vrow[d] = vn[d];
+                }
+            }
+        }
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)max_ctx);
+        if (!z) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t rh = 0; rh < (int64_t)T * H; ++rh) {
+                int32_t r = (int32_t)(rh / H), h = (int32_t)(rh % H), g = h / R;
+                int32_t b = 0; /* the sequence holding row r */
+                while (!(cu[b] <= r && r < cu[b + 1])) ++b;
+                int32_t p = offset[b] + (r - cu[b]); /* this query's position */
+                int32_t L = p + 1;                   /* keys 0 .. p are visible */
+                double qr[HD];
+                rope_head(q + (int64_t)r * q_stride + (int64_t)h * HD, cos_t, sin_t, p, qr);
+                const float* kb = k_cache + ((int64_t)b * G + g) * cap * HD;
+                const float* vb = v_cache + ((int64_t)b * G + g) * cap * HD;
+                double m = -INFINITY;
+                for (int32_t j = 0; j < L; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < HD; ++d) dot += qr[d] * (double)kb[(int64_t)j * HD + d];
+                    z[j] = scale * dot;
+                    if (z[j] > m) m = z[j];
+                }
+                double l = 0.0;
+                for (int32_t j = 0; j < L; ++j) {
+                    z[j] = exp(z[j] - m);
+                    l += z[j];
+                }
+                double o[HD];
+                for (int d = 0; d < HD; ++d) o[d] = 0.0;
+                for (int32_t j = 0; j < L; ++j) {
+                    double pj = z[j] / l;
+                    for (int d = 0; d < HD; ++d) o[d] += pj * (double)vb[(int64_t)j * HD + d];
+                }
+                float* orow = out + (int64_t)r * out_stride + (int64_t)h * HD;
+                for (int d = 0; d < HD; ++d) orow[d] = (float)o[d];
+            }
+        }
+        free(z);
+    }
+    return bad ? -1 : 0;
+}

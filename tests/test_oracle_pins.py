@@ -445,3 +445,106 @@ def test_binary16_rounding_step_is_round_to_nearest_even():
     with np.errstate(over="ignore"):  # 65520 rounds up to infinity, as the format says
         for x, bits in cases.items():
             assert int(np.float64(x).astype(np.float16).view(np.uint16)) == bits, x
+
+
+# ----------------------------------------------------------------------------- chunked prefill from a cache
+
+def _chunk_inputs(lengths, offsets, H, G, cap, seed):
+    rng = np.random.default_rng(seed)
+    B = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, H * D), dtype=np.float32)
+    k = rng.standard_normal((T, G * D), dtype=np.float32)
+    v = rng.standard_normal((T, G * D), dtype=np.float32)
+    kc = rng.standard_normal((B, G, cap, D), dtype=np.float32)
+    vc = rng.standard_normal((B, G, cap, D), dtype=np.float32)
+    return cu, np.array(offsets, np.int32), q, k, v, kc, vc
+
+
+def test_prefill_cached_one_row_chunks_are_decode_steps_bit_for_bit():
+    H, G, cap = 9, 3, 300
+    lengths, offsets = [1, 1, 1, 1], [0, 17, 128, 299]
+    cu, off, q, k, v, kc, vc = _chunk_inputs(lengths, offsets, H, G, cap, 41)
+    tables = oracle.rope_tables(1e5, cap)
+    a, ka, va = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G, tables=tables)
+    b, kb, vb = oracle.decode(q, k, v, kc, vc, off + 1, H, G, tables=tables)
+    assert np.array_equal(a, b) and np.array_equal(ka, kb) and np.array_equal(va, vb)
+
+
+def test_prefill_cached_two_chunks_equal_one_chunk_bit_for_bit():
+    H, G, cap = 4, 2, 400
+    n, split, off0 = 150, 61, 37
+    cu, off, q, k, v, kc, vc = _chunk_inputs([n], [off0], H, G, cap, 42)
+    tables = oracle.rope_tables(1e4, cap)
+    whole, kw, vw = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G, tables=tables)
+    o1, k1, v1 = oracle.prefill_cached(q[:split], k[:split], v[:split], [0, split], [off0], kc, vc,
+                                       H, G, tables=tables)
+    o2, k2, v2 = oracle.prefill_cached(q[split:], k[split:], v[split:], [0, n - split],
+                                       [off0 + split], k1, v1, H, G, tables=tables)
+    assert np.array_equal(np.concatenate([o1, o2]), whole)
+    assert np.array_equal(k2, kw) and np.array_equal(v2, vw)
+
+
+def test_prefill_cached_from_an_empty_cache_is_causal_attention():
+    # inputs already rotated: the stored keys are the inputs themselves, and the causal
+    # varlen definition (materialised -inf mask) gives the same bits
+    H, G, cap = 6, 2, 256
+    lengths = [70, 1, 200]
+    cu, off, q, k, v, kc, vc = _chunk_inputs(lengths, [0, 0, 0], H, G, cap, 43)
+    a, _, _ = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G)
+    b = oracle.varlen_attention(q, k, v, cu, H, G, -1, True)
+    assert np.array_equal(a, b)
+    # with rotation the cache holds f32-rounded keys: agreement to the rounding of k
+    tables = oracle.rope_tables(1e5, cap)
+    a, _, _ = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G, tables=tables)
+    b = oracle.varlen_attention(q, k, v, cu, H, G, -1, True, tables=tables)
+    assert np.max(np.abs(a - b)) <= 1e-6
+
+
+def test_prefill_cached_uniform_weights_recover_the_causal_range_with_offset():
+    # q = 0: key j <= p has weight 1/(p+1); v_j = [1, j, j^2] gives [1, p/2, p(2p+1)/6]
+    H, G, cap = 2, 1, 64
+    lengths, offsets = [5, 9, 1], [0, 20, 63]
+    cu, off, q, k, v, kc, vc = _chunk_inputs(lengths, offsets, H, G, cap, 44)
+    q[:] = 0.0
+    j = np.arange(cap, dtype=np.float32)
+    vc[:, :, :, :] = 0.0
+    vc[:, :, :, 0], vc[:, :, :, 1], vc[:, :, :, 2] = 1.0, j, j * j
+    v[:] = 0.0
+    for b in range(len(lengths)):
+        for i in range(lengths[b]):
+            p = offsets[b] + i
+            v[cu[b] + i, 0:3] = [1.0, p, p * p]
+    out, _, _ = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G)
+    for b in range(len(lengths)):
+        for i in range(lengths[b]):
+            p = offsets[b] + i
+            want = np.array([1.0, p / 2.0, p * (2 * p + 1) / 6.0])
+            for h in range(H):
+                got = out[cu[b] + i, h * D:h * D + 3].astype(np.float64)
+                assert np.allclose(got, want, rtol=1e-6, atol=0), (b, i, h)
+
+
+def test_prefill_cached_writes_exactly_the_chunk_rows():
+    H, G, cap = 4, 2, 128
+    lengths, offsets = [10, 0, 33], [5, 7, 95]
+    cu, off, q, k, v, kc, vc = _chunk_inputs(lengths, offsets, H, G, cap, 45)
+    tables = oracle.rope_tables(1e4, cap)
+    _, k2, v2 = oracle.prefill_cached(q, k, v, cu, off, kc, vc, H, G, tables=tables)
+    for b in range(3):
+        lo, n, o = int(cu[b]), lengths[b], offsets[b]
+        pos = np.arange(o, o + n, dtype=np.int32)
+        krot = oracle.rope_apply(k[lo:lo + n], G, pos, *tables) if n else np.zeros((0, G * D))
+        for g in range(G):
+            assert np.array_equal(k2[b, g, o:o + n], krot[:, g * D:(g + 1) * D])
+            assert np.array_equal(v2[b, g, o:o + n], v[lo:lo + n, g * D:(g + 1) * D])
+            rest = np.r_[0:o, o + n:cap]
+            assert np.array_equal(k2[b, g, rest], kc[b, g, rest])
+            assert np.array_equal(v2[b, g, rest], vc[b, g, rest])
+
+
+def test_prefill_cached_rejects_a_chunk_past_the_capacity():
+    cu, off, q, k, v, kc, vc = _chunk_inputs([10], [60], 2, 1, 64, 46)
+    with pytest.raises(ValueError):
+        oracle.prefill_cached(q, k, v, cu, off, kc, vc, 2, 1)
