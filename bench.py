@@ -15,6 +15,7 @@ runs on and the L2/MALL flushed between calls:
   prefill_causal_1142   SmolLM2 causal GQA prefill, one 1142-token sequence
   prefill_causal_16x2048 SmolLM2 causal GQA prefill, 16 x 2048
   decode_b64            SmolLM2 decode, 64 sequences, caches [64][3][8192][64]
+  chunked_prefill_b16   SmolLM2 prefill continuing from filled caches, 16 chunks
 
 `roofline` is for the headline step's dominant kernel (the attention tile
 kernel): algorithmic FLOPs per launch over its mean launch time.  `traffic`
@@ -37,7 +38,7 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 HEADLINE = "1"
 PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
-         "3b": "prefill_causal_16x2048", "4": "decode_b64"}
+         "3b": "prefill_causal_16x2048", "4": "decode_b64", "5": "chunked_prefill_b16"}
 
 
 def parse():
@@ -45,12 +46,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--parts", default="2,3a,3b,4",
+    ap.add_argument("--parts", default="2,3a,3b,4,5",
                     help="comma list of extra workloads to time, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 disables)")
     ap.add_argument("--only", default=None,
-                    help="run only this workload's loop (for profiling): 1, 2, 3a, 3b or 4")
+                    help="run only this workload's loop (for profiling): 1, 2, 3a, 3b, 4 or 5")
     ap.add_argument("--fused", action="store_true",
                     help="with --only: loop the fused-RoPE step instead of prologue + attention")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -139,6 +140,26 @@ def decode_part(torch, steps, warmup, flush):
            "decode_ms": round(mean_ms, 4), "decode_ms_min": round(min_ms, 4),
            "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del run
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_part(torch, steps, warmup, flush):
+    from transformer_attention_varlen_amd import metrics, workloads as wl
+    from transformer_attention_varlen_amd.session import ChunkRun
+    case = wl.build("5")
+    run = ChunkRun(case, rotate=True)
+    # every call appends the same chunk at the same rows, so repeated calls do equal work
+    mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
+    flops = metrics.chunk_flops(case.lengths, case.offsets, case.H)
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    res = {"workload": wl.WORKLOADS["5"].name, "seqs": case.B, "chunk_tokens": case.T,
+           "heads": case.H, "kv_heads": case.G, "cap": case.cap, "max_ctx": case.max_ctx,
+           "ms": round(mean_ms, 4), "ms_min": round(min_ms, 4),
+           "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
+           "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
+           "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4)}
     del run
     torch.cuda.empty_cache()
     return res
@@ -248,6 +269,10 @@ def main():
             from transformer_attention_varlen_amd.session import DecodeRun
             run = DecodeRun(wl.build("4"), rotate=True)
             fn = run.step
+        elif args.only == "5":
+            from transformer_attention_varlen_amd.session import ChunkRun
+            run = ChunkRun(wl.build("5"), rotate=True)
+            fn = run.step
         else:
             run = PrefillRun(wl.build(args.only))
             fn = run.step_fused if args.fused else run.step
@@ -326,6 +351,8 @@ def main():
             psteps, pwarm = max(5, args.steps // 2), 2
             if k == "4":
                 parts[PARTS[k]] = decode_part(torch, psteps, pwarm, flush)
+            elif k == "5":
+                parts[PARTS[k]] = chunk_part(torch, psteps, pwarm, flush)
             else:
                 parts[PARTS[k]] = prefill_part(torch, k, psteps, pwarm, flush)
         del flush

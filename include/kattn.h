@@ -183,6 +183,51 @@ int kattn_varlen_fwd_f16(void* out, int64_t out_stride, const float* q, int64_t 
                          const float* cos, const float* sin, int32_t table_len, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace kattn_prefill_cached needs for B sequences and T chunk rows. */
+size_t kattn_prefill_cached_workspace(int32_t B, int32_t T);
+
+/*
+ * Chunked prefill continuing from preallocated KV caches ([argus text.rs]
+ * `KvAppend` at the cache's fill point, then `CausalSoftmax` with q_len > 1
+ * and an offset, whose causal limit for query i is key offset + i; the GQA
+ * fold of `block`).  Sequence b brings n_b = cu[b+1] - cu[b] new rows (packed
+ * rows cu[b] .. cu[b+1]-1 of q, k_new, v_new) and already holds off_b =
+ * offset[b] rows.  With p = off_b + i for chunk row i:
+ *   1. k_new row i (rotated at p when cos != NULL) and v_new row i are
+ *      written into cache row p of every kv head of b; no other cache row is
+ *      written;
+ *   2. q row i (rotated at p when cos != NULL, scaled by `scale`; q itself is
+ *      not modified) attends, head h through kv head h / (H/G), to cache rows
+ *      0 .. p: out[cu[b]+i][64h..] = sum_j softmax_j(scale <q, k_j>) v_j.
+ * Decode is the case n_b = 1 (kattn_decode does it with a split over keys).
+ *   out:        device float (T, H*64), row stride out_stride.
+ *   q:          device float (T, H*64), row stride q_stride.
+ *   k_new, v_new: device float (T, G*64) with their strides.
+ *   cu:         device int32[B+1], chunk offsets (as kattn_build_index checks them).
+ *   offset:     device int32[B], rows already in each sequence's caches.
+ *   max_chunk:  host, the longest chunk (<= T); max_ctx: host, max of
+ *               offset[b] + n_b, with max_chunk <= max_ctx <= cap.
+ *   k_cache, v_cache: device float [B][G][cap][64] (the kattn_decode layout).
+ *   cos, sin:   device float[table_len][32], table_len >= max_ctx, or both
+ *               NULL when q and k_new are already rotated.
+ *   workspace:  device, >= kattn_prefill_cached_workspace(B, T) bytes,
+ *               256-byte aligned.
+ * Preconditions on the device tables: 0 <= offset[b], offset[b] + n_b <=
+ * max_ctx, n_b <= max_chunk.  The kernels stay inside every buffer when they
+ * do not hold (rows past the cache are not appended; keys are clamped to the
+ * cache), but the results are then unspecified; KATTN_CHECK=1 validates them.
+ * T == 0 or B == 0 queues nothing.
+ * Errors: EINVAL, EUNSUPPORTED (head_dim, H % G, alignment, B > 65535),
+ * EBOUNDS (max_chunk, max_ctx, cap, table_len, strides, workspace), EDEVICE.
+ */
+int kattn_prefill_cached(float* out, int64_t out_stride, const float* q, int64_t q_stride,
+                         const float* k_new, int64_t k_stride, const float* v_new, int64_t v_stride,
+                         const int32_t* cu, const int32_t* offset, int32_t B, int32_t T,
+                         int32_t max_chunk, int32_t max_ctx, float* k_cache, float* v_cache,
+                         int32_t cap, int32_t H, int32_t G, int32_t head_dim, float scale,
+                         const float* cos, const float* sin, int32_t table_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace kattn_decode needs for B sequences, H q heads and G kv
  * heads (0 for invalid sizes).  The size does not depend on the cache lengths. */
 size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(kattn.EXPORTS)
     L = kattn.lib()
     for n in names:
@@ -227,3 +227,41 @@ def test_decode_workspace_size():
     assert a >= (8192 + 64 * 3) * 3 * 66 * 4
     assert kattn.kattn_decode_workspace(64, 9, 2) == 0
     assert kattn.kattn_decode_workspace(-1, 9, 3) == 0
+
+
+def _chunk(**kw):
+    a = dict(out=P(256), out_stride=576, q=P(256), q_stride=576, k_new=P(256), k_stride=192,
+             v_new=P(256), v_stride=192, cu=P(256), offset=P(256), B=2, T=100, max_chunk=60,
+             max_ctx=300, k_cache=P(4096), v_cache=P(4096), cap=512, H=9, G=3, head_dim=64,
+             scale=0.125, cos=P(512), sin=P(512), table_len=512, workspace=P(4096),
+             workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return kattn.lib().kattn_prefill_cached(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), kattn.KATTN_EUNSUPPORTED),
+    (dict(G=2), kattn.KATTN_EUNSUPPORTED),
+    (dict(B=-1), kattn.KATTN_EINVAL),
+    (dict(cap=0), kattn.KATTN_EINVAL),
+    (dict(max_chunk=101), kattn.KATTN_EBOUNDS),
+    (dict(max_ctx=513), kattn.KATTN_EBOUNDS),
+    (dict(max_ctx=59), kattn.KATTN_EBOUNDS),
+    (dict(table_len=299), kattn.KATTN_EBOUNDS),
+    (dict(sin=None), kattn.KATTN_EINVAL),
+    (dict(offset=None), kattn.KATTN_EINVAL),
+    (dict(k_cache=P(4100)), kattn.KATTN_EUNSUPPORTED),
+    (dict(q_stride=500), kattn.KATTN_EBOUNDS),
+    (dict(workspace_bytes=16), kattn.KATTN_EBOUNDS),
+    (dict(B=70000, T=70000, max_chunk=1, max_ctx=1), kattn.KATTN_EUNSUPPORTED),
+])
+def test_prefill_cached_rejects_bad_arguments_on_the_host(kw, code):
+    assert _chunk(**kw) == code
+    assert kattn.lib().kattn_last_error()
+
+
+def test_prefill_cached_empty_batch_queues_nothing():
+    assert _chunk(T=0, max_chunk=0, out=None, q=None) == kattn.KATTN_OK
+    assert _chunk(B=0, T=0, max_chunk=0, cos=None, sin=None, table_len=0) == kattn.KATTN_OK
+    assert kattn.lib().kattn_last_error() == b""
+    assert kattn.kattn_prefill_cached_workspace(16, 9944) == kattn.kattn_varlen_fwd_workspace(16, 9944)

@@ -382,3 +382,97 @@ def test_f16_output_headline_workload():
                                     out_dtype=np.float64)
     err = np.abs(got[rows].astype(np.float64) - ref64)
     assert np.all(err <= _f16_bound(ref64, got[rows]))
+
+
+# ----------------------------------------------------------------------------- chunked prefill from a cache
+
+from transformer_attention_varlen_amd.session import ChunkRun  # noqa: E402
+
+
+def _check_chunk(case, rotate, pad_rows=3):
+    run = ChunkRun(case, rotate=rotate, out_pad_rows=pad_rows)
+    run.out_full.fill_(float("nan"))
+    run.step()
+    torch.cuda.synchronize()
+    tables = oracle.rope_tables(case.theta, case.cap) if rotate else None
+    ref, kc, vc = oracle.prefill_cached(case.q, case.k, case.v, case.cu, case.offsets,
+                                        case.k_cache, case.v_cache, case.H, case.G, tables=tables,
+                                        threads=16)
+    got = run.out_full.cpu().numpy()
+    assert max_err(got[:case.T], ref) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))  # rows past T are never written
+    gk, gv = run.k_cache.cpu().numpy(), run.v_cache.cpu().numpy()
+    for b in range(case.B):
+        o, n = int(case.offsets[b]), int(case.lengths[b])
+        assert max_err(gk[b, :, o:o + n], kc[b, :, o:o + n]) <= ROPE_ATOL
+        assert np.array_equal(gv[b, :, o:o + n], vc[b, :, o:o + n])
+        gk[b, :, o:o + n] = kc[b, :, o:o + n]
+    # every other cache row is untouched
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    # q, k and v are read-only
+    assert np.array_equal(run.q.cpu().numpy(), case.q)
+    assert np.array_equal(run.k.cpu().numpy(), case.k)
+    return run
+
+
+CHUNK_CASES = [
+    # lengths, offsets, H, G, cap
+    ([1, 31, 32, 33, 129], [0, 0, 5, 100, 200], 9, 3, 400),
+    ([200, 0, 64, 1], [0, 17, 300, 399], 4, 4, 400),
+    ([150, 77], [250, 323], 8, 2, 400),        # chunks that end at the last cache row
+    ([300], [0], 6, 2, 300),                   # a fresh cache filled exactly
+    ([65, 2, 127], [1, 63, 128], 5, 1, 256),
+]
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("lengths,offsets,H,G,cap", CHUNK_CASES)
+def test_prefill_cached_small_cases(rotate, lengths, offsets, H, G, cap):
+    case = wl.make_chunked(lengths, offsets, H, G, cap, theta=1e5, seed=500 + H + cap)
+    _check_chunk(case, rotate)
+
+
+def test_prefill_cached_full_workload():
+    _check_chunk(wl.build("5"), rotate=True, pad_rows=0)
+
+
+def test_prefill_cached_two_chunks_match_one():
+    H, G, cap, n, split, off0 = 9, 3, 1024, 500, 173, 211
+    one = wl.make_chunked([n], [off0], H, G, cap, seed=61)
+    r1 = ChunkRun(one)
+    r1.step()
+    torch.cuda.synchronize()
+    a = wl.ChunkCase("a", np.array([split], np.int32), np.array([0, split], np.int32),
+                     np.array([off0], np.int32), H, G, cap, one.theta, one.k_cache, one.v_cache,
+                     one.q[:split], one.k[:split], one.v[:split])
+    ra = ChunkRun(a)
+    ra.step()
+    torch.cuda.synchronize()
+    b = wl.ChunkCase("b", np.array([n - split], np.int32), np.array([0, n - split], np.int32),
+                     np.array([off0 + split], np.int32), H, G, cap, one.theta,
+                     ra.k_cache.cpu().numpy(), ra.v_cache.cpu().numpy(), one.q[split:],
+                     one.k[split:], one.v[split:])
+    rb = ChunkRun(b)
+    rb.step()
+    torch.cuda.synchronize()
+    both = np.concatenate([ra.out.cpu().numpy(), rb.out.cpu().numpy()])
+    assert max_err(both, r1.out.cpu().numpy()) <= ATOL
+    assert torch.equal(rb.k_cache.cpu(), r1.k_cache.cpu())
+    assert torch.equal(rb.v_cache.cpu(), r1.v_cache.cpu())
+
+
+def test_prefill_cached_one_row_chunks_match_decode():
+    H, G, cap = 9, 3, 520
+    used = np.array([1, 2, 255, 256, 257, 300, 513], np.int32)
+    dec = _decode_case(used, H, G, cap, seed=62)
+    d = DecodeRun(dec, rotate=True)
+    d.step()
+    B = len(used)
+    ch = wl.ChunkCase("c", np.ones(B, np.int32), np.arange(B + 1, dtype=np.int32), used - 1, H, G,
+                      cap, dec.theta, dec.k_cache, dec.v_cache, dec.q_new, dec.k_new, dec.v_new)
+    c = ChunkRun(ch)
+    c.step()
+    torch.cuda.synchronize()
+    assert max_err(c.out.cpu().numpy(), d.out.cpu().numpy()) <= ATOL
+    assert torch.equal(c.v_cache.cpu(), d.v_cache.cpu())
+    assert max_err(c.k_cache.cpu().numpy(), d.k_cache.cpu().numpy()) <= ROPE_ATOL

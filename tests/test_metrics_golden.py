@@ -60,3 +60,11 @@ def test_decode_bytes():
     used = np.array([1143, 8192])
     b = metrics.decode_bytes(used, 9, 3)
     assert b == 1536 * (1142 + 8191) + 2 * (9 * 256 + 4 * 768 + 9 * 256)
+
+
+def test_chunk_pairs_count_every_visible_cache_row():
+    # brute force over the rows: query i of a chunk after `off` filled rows sees off + i + 1 keys
+    lengths, offsets = [3, 0, 7, 1], [0, 5, 12, 99]
+    brute = sum(o + i + 1 for n, o in zip(lengths, offsets) for i in range(n))
+    assert metrics.chunk_pairs_per_head(lengths, offsets) == brute
+    assert metrics.chunk_flops(lengths, offsets, 9) == 256 * 9 * brute

@@ -76,7 +76,19 @@ __device__ inline SeqRange seq_range(const int32_t* cu, int s, int T) {
     return {lo, max(hi - lo, 0)};
 }
 
-// Key range [kbeg, kend) a block of query rows [q0, qend) may see, kbeg
+// Keys of sequence s: its own n rows (packed), or, continuing from a KV cache, the cache rows
+// 0 .. off+n-1 where off = kv_off[s] rows were filled before this chunk (clamped to the cache,
+// so a malformed offset never reads outside it).
+__device__ inline void key_count(const int32_t* kv_off, int cap, int s, int n, int& off, int& nk) {
+    off = 0;
+    nk = n;
+    if (kv_off != nullptr) {
+        off = min(max(kv_off[s], 0), cap);
+        nk = min(off + n, cap);
+    }
+}
+
+// Key range [kbeg, kend) a block of query positions [q0, qend) may see among nk keys, kbeg
 // aligned down to BN from the sequence start.  hw < 0: no window.
 __device__ inline void key_range(int q0, int qend, int n, int hw, int causal, int& kbeg,
                                  int& kend) {
@@ -122,6 +134,8 @@ __device__ inline int block_scan(int v, int* wave_sums, int* total) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S,
                                                            int T, int BM, int hw, int causal,
+                                                           const int32_t* __restrict__ kv_off,
+                                                           int cap,
                                                            int32_t* __restrict__ ws_prefix,
                                                            int2* __restrict__ tiles,
                                                            int32_t* __restrict__ count,
@@ -166,8 +180,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
             const int s = lo;
             const int n = in_lds ? lds_len[s] : seq_range(cu, s, T).n;
             const int q0 = (t - pre[s]) * BM;
+            int off, nk;
+            key_count(kv_off, cap, s, n, off, nk);
             int kb, ke;
-            key_range(q0, min(q0 + BM, n), n, hw, causal, kb, ke);
+            key_range(off + q0, off + min(q0 + BM, n), nk, hw, causal, kb, ke);
             const int work = ke > kb ? (ke - kb + BN - 1) / BN : 0;
             const int bin = min(work, kPlanBins - 1);
             if (pass == 0) {
@@ -209,9 +225,13 @@ struct FwdParams {
     const int2* tiles;
     const int32_t* count;
     int64_t out_stride, q_stride, k_stride, v_stride;
-    const float* cos_t;  // RoPE tables [table_len][32] for the fused-rotation variant
+    const float* cos_t;  // RoPE tables [table_len][32] for the fused-rotation variants
     const float* sin_t;
     int table_len;
+    // continuing from a KV cache: per-sequence filled rows, the cache [S][G][cap][64]
+    const int32_t* kv_off;   // nullptr: keys are the packed rows of the sequence itself
+    int64_t kv_head_stride;  // floats between kv heads: 64 (packed rows) or cap * 64 (cache)
+    int G, cap;
     int T, H, R, nunits, hw, causal;
     float scale;
 };
@@ -226,14 +246,16 @@ __device__ inline float ror8(float x) {
 // round, fewer barriers per flop).  Banded launches (a window or a causal limit) use 32-key
 // tiles: a wave's band is covered with less waste, and half the score and staging registers
 // leave room for a third wave per SIMD.
-// ROPE: q and k arrive unrotated; q is rotated as it is loaded and every K row as it is
-// staged in LDS, at its position inside the sequence (the RoPE step of kime-cpu plan.rs
-// `Ctx::step` and argus text.rs `rope`, moved into the tile loads).
+// ROT: 0, q and k arrive rotated; 1, q and k arrive unrotated: q is rotated as it is loaded
+// and every K row as it is staged in LDS, at its position inside the sequence (the RoPE step
+// of kime-cpu plan.rs `Ctx::step` and argus text.rs `rope`, moved into the tile loads); 2,
+// only q is rotated (keys come from a cache that holds rotated rows).
 // F16: the output is written as IEEE binary16 (round to nearest even) instead of FP32.
-template <int HPW, int QW, int TBN, bool ROPE, bool F16>
+template <int HPW, int QW, int TBN, int ROT, bool F16>
 __global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(TBN == 32 ? 3 : 2)))
 void fwd_kernel(FwdParams p) {
     static_assert(TBN == 32 || TBN == 64, "tiles hold one or two 32-key score blocks");
+    constexpr bool ROPE_Q = ROT != 0, ROPE_K = ROT == 1;
     constexpr int NT = 64 * HPW * QW;
     constexpr int BM = 32 * QW;
     constexpr bool TWO = TBN == 64;
@@ -246,6 +268,8 @@ void fwd_kernel(FwdParams p) {
     const int2 tile = p.tiles[tix];
     const SeqRange sr = seq_range(p.cu, tile.x, p.T);
     const int lo = sr.lo, n = sr.n, q0 = tile.y;
+    int off, nk;  // query row i sits at position off + i; keys 0 .. nk-1
+    key_count(p.kv_off, p.cap, tile.x, n, off, nk);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -257,6 +281,7 @@ void fwd_kernel(FwdParams p) {
     const int qi = qa + j;                  // this lane's query
     const bool wave_live = qa < n;
     const int qlast_w = min(qa + 31, n - 1);
+    const int pa = off + qa, plast_w = off + qlast_w, pq = off + qi;  // positions
 
     f32x16 O0, O1;  // O^T accumulators: rows i -> dims 2i (O0) and 2i+1 (O1), column = query j
 #pragma unroll
@@ -268,11 +293,19 @@ void fwd_kernel(FwdParams p) {
     float l_run = 0.0f;     // running sum over this lane half's keys
 
     int kbeg, kend;
-    key_range(q0, min(q0 + BM, n), n, p.hw, p.causal, kbeg, kend);
+    key_range(off + q0, off + min(q0 + BM, n), nk, p.hw, p.causal, kbeg, kend);
     kbeg = (kbeg / TBN) * TBN;
 
-    const float* kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
-    const float* vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
+    const float* kbase;
+    const float* vbase;
+    if (p.kv_off != nullptr) {  // cache rows of kv head g of sequence tile.x
+        const int64_t h0 = (static_cast<int64_t>(tile.x) * p.G + g) * p.kv_head_stride;
+        kbase = p.k + h0;
+        vbase = p.v + h0;
+    } else {
+        kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
+        vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
+    }
 
     // K/V tiles are staged through LDS.  The next tile's rows are loaded into registers
     // before this tile's MFMA work and written to LDS after it, so the global-load latency
@@ -291,23 +324,23 @@ void fwd_kernel(FwdParams p) {
 #define KATTN_TAB(R) (reinterpret_cast<const float4*>(tab + min(R, static_cast<int64_t>(p.table_len) - 1) * 32)[0])
 #define KATTN_FETCH(K0)                                                                         \
     {                                                                                           \
-        const int64_t r0 = min((K0) + lrow, n - 1), r1 = min((K0) + lrow + rstep, n - 1);       \
+        const int64_t r0 = min((K0) + lrow, nk - 1), r1 = min((K0) + lrow + rstep, nk - 1);     \
         pk0 = reinterpret_cast<const float4*>(kbase + r0 * p.k_stride)[lcol];                  \
         pk1 = reinterpret_cast<const float4*>(kbase + r1 * p.k_stride)[lcol];                  \
         pv0 = reinterpret_cast<const float4*>(vbase + r0 * p.v_stride)[lcol];                  \
         pv1 = reinterpret_cast<const float4*>(vbase + r1 * p.v_stride)[lcol];                  \
-        if constexpr (ROPE) {                                                                   \
+        if constexpr (ROPE_K) {                                                                 \
             pt0 = KATTN_TAB(r0);                                                                \
             pt1 = KATTN_TAB(r1);                                                                \
         }                                                                                       \
         if constexpr (TWO) {                                                                    \
-            const int64_t r2 = min((K0) + lrow + 2 * rstep, n - 1);                             \
-            const int64_t r3 = min((K0) + lrow + 3 * rstep, n - 1);                             \
+            const int64_t r2 = min((K0) + lrow + 2 * rstep, nk - 1);                            \
+            const int64_t r3 = min((K0) + lrow + 3 * rstep, nk - 1);                            \
             pk2 = reinterpret_cast<const float4*>(kbase + r2 * p.k_stride)[lcol];              \
             pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];              \
             pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];              \
             pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];              \
-            if constexpr (ROPE) {                                                               \
+            if constexpr (ROPE_K) {                                                             \
                 pt2 = KATTN_TAB(r2);                                                            \
                 pt3 = KATTN_TAB(r3);                                                            \
             }                                                                                   \
@@ -316,7 +349,7 @@ void fwd_kernel(FwdParams p) {
     // rotate a staged K piece: x[i] c - x[i+32] s in the low lanes, x[i+32] c + x[i] s in the
     // high lanes (the other half of each pair and the other table come from lane ^ 8)
 #define KATTN_ROT(X, TT)                                                                        \
-    if constexpr (ROPE) {                                                                       \
+    if constexpr (ROPE_K) {                                                                       \
         const float4 y = make_float4(ror8(X.x), ror8(X.y), ror8(X.z), ror8(X.w));               \
         const float4 u = make_float4(ror8(TT.x), ror8(TT.y), ror8(TT.z), ror8(TT.w));           \
         if (lcol < 8) {                                                                         \
@@ -356,11 +389,11 @@ void fwd_kernel(FwdParams p) {
     if (qi < n) {
         const float* qrow = p.q + static_cast<int64_t>(lo + qi) * p.q_stride + head * kHeadDim;
         const float4* src = reinterpret_cast<const float4*>(qrow + hh * 32);
-        if constexpr (ROPE) {
-            // pairs (x[i], x[i+32]) at position qi: the low lane half loads dims 0..31 and the
+        if constexpr (ROPE_Q) {
+            // pairs (x[i], x[i+32]) at position pq: the low lane half loads dims 0..31 and the
             // cos row, the high half dims 32..63 and the sin row; a permlane32 swap then gives
             // every lane both members of each pair and both tables (low value first).
-            const int64_t prow = min(qi, p.table_len - 1);
+            const int64_t prow = min(pq, p.table_len - 1);
             const float4* tq = reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
             float4 xa[8], ta[8];
 #pragma unroll
@@ -407,15 +440,15 @@ void fwd_kernel(FwdParams p) {
 
         // Does this wave see some key of the tile, and does it see every one of them?
         const int klast = kt + TBN - 1;
-        bool any = wave_live && kt < n;
-        bool full = wave_live && klast < n;
+        bool any = wave_live && kt < nk;
+        bool full = wave_live && klast < nk;
         if (p.causal) {
-            any = any && kt <= qlast_w;
-            full = full && klast <= qa;
+            any = any && kt <= plast_w;
+            full = full && klast <= pa;
         }
         if (p.hw >= 0) {
-            any = any && kt <= qlast_w + p.hw && klast >= qa - p.hw;
-            full = full && kt >= qlast_w - p.hw && klast <= qa + p.hw;
+            any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
+            full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
         if (any) {
             // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
@@ -449,14 +482,14 @@ void fwd_kernel(FwdParams p) {
                 for (int r = 0; r < 16; ++r) {
                     const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
                     const int key1 = key0 + 32;
-                    bool v0 = key0 < n, v1 = key1 < n;
+                    bool v0 = key0 < nk, v1 = key1 < nk;
                     if (p.causal) {
-                        v0 = v0 && key0 <= qi;
-                        v1 = v1 && key1 <= qi;
+                        v0 = v0 && key0 <= pq;
+                        v1 = v1 && key1 <= pq;
                     }
                     if (p.hw >= 0) {
-                        v0 = v0 && abs(qi - key0) <= p.hw;
-                        v1 = v1 && abs(qi - key1) <= p.hw;
+                        v0 = v0 && abs(pq - key0) <= p.hw;
+                        v1 = v1 && abs(pq - key1) <= p.hw;
                     }
                     if (!v0) S0[r] = -INFINITY;
                     if (TWO && !v1) S1[r] = -INFINITY;
@@ -571,21 +604,67 @@ Shape pick_shape(int R) {
     }
 }
 
-template <int HPW, int QW, bool ROPE, bool F16>
+template <int HPW, int QW, int ROT, bool F16>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
     if (p.causal || p.hw >= 0)
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32, ROPE, F16>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32, ROT, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64, ROPE, F16>), dim3(static_cast<unsigned>(grid)),
+    else if constexpr (ROT != 2)  // keys from a cache are always causal
+        hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64, ROT, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
 }
 
-template <bool ROPE, bool F16>
+template <int ROT, bool F16>
 void launch_shape(const Shape& sh, const FwdParams& p, int64_t grid, hipStream_t stream) {
-    if (sh.hpw == 1) launch_fwd<1, 4, ROPE, F16>(p, grid, stream);
-    else if (sh.hpw == 2) launch_fwd<2, 2, ROPE, F16>(p, grid, stream);
-    else launch_fwd<4, 1, ROPE, F16>(p, grid, stream);
+    if (sh.hpw == 1) launch_fwd<1, 4, ROT, F16>(p, grid, stream);
+    else if (sh.hpw == 2) launch_fwd<2, 2, ROT, F16>(p, grid, stream);
+    else launch_fwd<4, 1, ROT, F16>(p, grid, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Chunk append for prefill continuing from a KV cache (argus text.rs `KvAppend` at the cache's
+// fill point): row i of sequence b's chunk goes to cache row off + i of every kv head, its key
+// rotated at position off + i.  8 threads per (row, kv head), 4 pairs each, 16-byte accesses;
+// grid.y is the sequence, grid.x covers the longest chunk.
+constexpr int kAppendBlock = 256;
+
+__global__ __launch_bounds__(kAppendBlock) void append_kernel(
+    float* __restrict__ k_cache, float* __restrict__ v_cache, const float* __restrict__ k_new,
+    int64_t k_stride, const float* __restrict__ v_new, int64_t v_stride,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_off, int T, int G, int cap,
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, int table_len) {
+    const int b = blockIdx.y;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kAppendBlock + threadIdx.x;
+    const int i = static_cast<int>(idx / (8 * G));
+    const int rem = static_cast<int>(idx - static_cast<int64_t>(i) * 8 * G);
+    const int g = rem >> 3, t = rem & 7;
+    const SeqRange sr = seq_range(cu, b, T);
+    if (i >= sr.n) return;
+    const int off = kv_off[b];
+    if (off < 0 || off > cap - 1 - i) return;  // the row would fall outside the cache
+    const int pos = off + i;
+    const float* x = k_new + static_cast<int64_t>(sr.lo + i) * k_stride + g * kHeadDim;
+    const float4 a = reinterpret_cast<const float4*>(x)[t];       // x[4t .. 4t+3]
+    const float4 c2 = reinterpret_cast<const float4*>(x + 32)[t];  // x[32+4t .. 32+4t+3]
+    float4 ra = a, rb = c2;
+    if (cos_t != nullptr && pos < table_len) {
+        const float4 c = reinterpret_cast<const float4*>(cos_t + static_cast<int64_t>(pos) * 32)[t];
+        const float4 sn = reinterpret_cast<const float4*>(sin_t + static_cast<int64_t>(pos) * 32)[t];
+        ra.x = a.x * c.x - c2.x * sn.x;
+        ra.y = a.y * c.y - c2.y * sn.y;
+        ra.z = a.z * c.z - c2.z * sn.z;
+        ra.w = a.w * c.w - c2.w * sn.w;
+        rb.x = c2.x * c.x + a.x * sn.x;
+        rb.y = c2.y * c.y + a.y * sn.y;
+        rb.z = c2.z * c.z + a.z * sn.z;
+        rb.w = c2.w * c.w + a.w * sn.w;
+    }
+    const int64_t dst = ((static_cast<int64_t>(b) * G + g) * cap + pos) * kHeadDim;
+    reinterpret_cast<float4*>(k_cache + dst)[t] = ra;
+    reinterpret_cast<float4*>(k_cache + dst + 32)[t] = rb;
+    const float* vs = v_new + static_cast<int64_t>(sr.lo + i) * v_stride + g * kHeadDim;
+    reinterpret_cast<float4*>(v_cache + dst)[t] = reinterpret_cast<const float4*>(vs)[t];
+    reinterpret_cast<float4*>(v_cache + dst + 32)[t] = reinterpret_cast<const float4*>(vs + 32)[t];
 }
 
 }  // namespace
@@ -626,6 +705,7 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     if (rope && table_len < max_seqlen)
         return fail(KATTN_EBOUNDS, "%s: table_len %d < max_seqlen %d", fn, table_len, max_seqlen);
     if (T == 0 || S == 0) return ok();
+    if (rope && table_len < 1) return fail(KATTN_EBOUNDS, "%s: empty RoPE tables", fn);
     if (!out || !q || !k || !v || !cu || !workspace) return fail(KATTN_EINVAL, "%s: null pointer", fn);
     if (out_stride < static_cast<int64_t>(H) * kHeadDim || q_stride < static_cast<int64_t>(H) * kHeadDim ||
         k_stride < static_cast<int64_t>(G) * kHeadDim || v_stride < static_cast<int64_t>(G) * kHeadDim)
@@ -669,7 +749,7 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     int2* tiles = reinterpret_cast<int2*>(ws + kHeader + prefix_bytes(S));
 
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw, causal,
-                       prefix, tiles, count, capacity);
+                       static_cast<const int32_t*>(nullptr), 0, prefix, tiles, count, capacity);
     int rc = check_launch(fn);
     if (rc != KATTN_OK) return rc;
 
@@ -688,6 +768,10 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.cos_t = cos;
     p.sin_t = sin;
     p.table_len = rope ? table_len : 0;
+    p.kv_off = nullptr;
+    p.kv_head_stride = kHeadDim;
+    p.G = G;
+    p.cap = 0;
     p.T = T;
     p.H = H;
     p.R = R;
@@ -695,10 +779,10 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.hw = hw;
     p.causal = causal;
     p.scale = scale;
-    if (rope && out_f16) launch_shape<true, true>(sh, p, grid, stream);
-    else if (rope) launch_shape<true, false>(sh, p, grid, stream);
-    else if (out_f16) launch_shape<false, true>(sh, p, grid, stream);
-    else launch_shape<false, false>(sh, p, grid, stream);
+    if (rope && out_f16) launch_shape<1, true>(sh, p, grid, stream);
+    else if (rope) launch_shape<1, false>(sh, p, grid, stream);
+    else if (out_f16) launch_shape<0, true>(sh, p, grid, stream);
+    else launch_shape<0, false>(sh, p, grid, stream);
     return check_launch(fn);
 }
 
@@ -740,4 +824,127 @@ extern "C" int kattn_varlen_fwd_f16(void* out, int64_t out_stride, const float* 
     return varlen_fwd("kattn_varlen_fwd_f16", out, out_stride, q, q_stride, k, k_stride, v,
                       v_stride, cu, S, T, max_seqlen, H, G, head_dim, window, causal, scale, cos,
                       sin, table_len, true, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t kattn_prefill_cached_workspace(int32_t B, int32_t T) {
+    return kattn_varlen_fwd_workspace(B, T);
+}
+
+extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float* q,
+                                    int64_t q_stride, const float* k_new, int64_t k_stride,
+                                    const float* v_new, int64_t v_stride, const int32_t* cu,
+                                    const int32_t* offset, int32_t B, int32_t T, int32_t max_chunk,
+                                    int32_t max_ctx, float* k_cache, float* v_cache, int32_t cap,
+                                    int32_t H, int32_t G, int32_t head_dim, float scale,
+                                    const float* cos, const float* sin, int32_t table_len,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kattn_prefill_cached";
+    if (head_dim != kHeadDim)
+        return fail(KATTN_EUNSUPPORTED, "%s: head_dim %d, only 64 is supported", fn, head_dim);
+    if (B < 0 || T < 0 || H < 1 || G < 1)
+        return fail(KATTN_EINVAL, "%s: B=%d T=%d H=%d G=%d", fn, B, T, H, G);
+    if (H % G != 0) return fail(KATTN_EUNSUPPORTED, "%s: H=%d is not a multiple of G=%d", fn, H, G);
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(KATTN_EINVAL, "%s: scale must be finite and > 0", fn);
+    if (cap < 1) return fail(KATTN_EINVAL, "%s: cap %d < 1", fn, cap);
+    if (max_chunk < 0 || max_chunk > T)
+        return fail(KATTN_EBOUNDS, "%s: max_chunk %d outside [0, T=%d]", fn, max_chunk, T);
+    if (max_ctx < max_chunk || max_ctx > cap)
+        return fail(KATTN_EBOUNDS, "%s: max_ctx %d outside [max_chunk=%d, cap=%d]", fn, max_ctx,
+                    max_chunk, cap);
+    if ((cos == nullptr) != (sin == nullptr))
+        return fail(KATTN_EINVAL, "%s: cos and sin must both be given or both be NULL", fn);
+    if (cos != nullptr && table_len < max_ctx)
+        return fail(KATTN_EBOUNDS, "%s: table_len %d < max_ctx %d", fn, table_len, max_ctx);
+    if (B > 65535) return fail(KATTN_EUNSUPPORTED, "%s: B=%d above the grid limit", fn, B);
+    if (T == 0 || B == 0) return ok();
+    if (cos != nullptr && table_len < 1) return fail(KATTN_EBOUNDS, "%s: empty RoPE tables", fn);
+    if (!out || !q || !k_new || !v_new || !cu || !offset || !k_cache || !v_cache || !workspace)
+        return fail(KATTN_EINVAL, "%s: null pointer", fn);
+    if (out_stride < static_cast<int64_t>(H) * kHeadDim || q_stride < static_cast<int64_t>(H) * kHeadDim ||
+        k_stride < static_cast<int64_t>(G) * kHeadDim || v_stride < static_cast<int64_t>(G) * kHeadDim)
+        return fail(KATTN_EBOUNDS, "%s: a row stride is narrower than its heads", fn);
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(k_cache) || !aligned16(v_cache) || (out_stride & 3) || (q_stride & 3) ||
+        (k_stride & 3) || (v_stride & 3) || (cos && (!aligned16(cos) || !aligned16(sin))))
+        return fail(KATTN_EUNSUPPORTED, "%s: pointers and strides must be multiples of 16 bytes", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+    const size_t need = kattn_prefill_cached_workspace(B, T);
+    if (workspace_bytes < need)
+        return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+    if (debug_checks()) {
+        std::vector<int32_t> h(static_cast<size_t>(B) + 1), o(static_cast<size_t>(B));
+        if (hipMemcpy(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(o.data(), offset, sizeof(int32_t) * o.size(), hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(KATTN_EDEVICE, "%s: KATTN_CHECK copy of cu / offset failed", fn);
+        if (h[0] != 0 || h[B] != T) return fail(KATTN_EBOUNDS, "%s: cu[0]=%d cu[B]=%d T=%d", fn, h[0], h[B], T);
+        for (int32_t b = 0; b < B; ++b) {
+            const int32_t n = h[b + 1] - h[b];
+            if (n < 0 || n > max_chunk) return fail(KATTN_EBOUNDS, "%s: chunk %d has %d rows", fn, b, n);
+            if (o[b] < 0 || static_cast<int64_t>(o[b]) + n > max_ctx)
+                return fail(KATTN_EBOUNDS, "%s: offset[%d]=%d + %d rows > max_ctx %d", fn, b, o[b], n, max_ctx);
+        }
+    }
+    if (static_cast<int64_t>(B) * G * cap * kHeadDim >= (int64_t(1) << 62))
+        return fail(KATTN_EBOUNDS, "%s: cache too large", fn);
+
+    // 1. the chunk's rotated keys and its values into the cache
+    if (max_chunk > 0) {
+        const int64_t threads = static_cast<int64_t>(max_chunk) * G * 8;
+        const dim3 grid(static_cast<unsigned>((threads + kAppendBlock - 1) / kAppendBlock),
+                        static_cast<unsigned>(B));
+        hipLaunchKernelGGL(append_kernel, grid, dim3(kAppendBlock), 0, stream, k_cache, v_cache,
+                           k_new, k_stride, v_new, v_stride, cu, offset, T, G, cap, cos, sin,
+                           cos ? table_len : 0);
+        const int rc = check_launch(fn);
+        if (rc != KATTN_OK) return rc;
+    }
+
+    // 2. the chunk's queries against cache rows 0 .. offset + i (causal with an offset)
+    const int R = H / G;
+    const Shape sh = pick_shape(R);
+    const int BM = 32 * sh.qw;
+    const int64_t capacity = tile_capacity(B, T, BM);
+    const int nunits = H / sh.hpw;
+    const int64_t grid = capacity * nunits;
+    if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* count = reinterpret_cast<int32_t*>(ws);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
+    int2* tiles = reinterpret_cast<int2*>(ws + kHeader + prefix_bytes(B));
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, B, T, BM, -1, 1,
+                       offset, cap, prefix, tiles, count, capacity);
+    int rc = check_launch(fn);
+    if (rc != KATTN_OK) return rc;
+
+    FwdParams p;
+    p.out = out;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.cu = cu;
+    p.tiles = tiles;
+    p.count = count;
+    p.out_stride = out_stride;
+    p.q_stride = q_stride;
+    p.k_stride = kHeadDim;
+    p.v_stride = kHeadDim;
+    p.cos_t = cos;
+    p.sin_t = sin;
+    p.table_len = cos ? table_len : 0;
+    p.kv_off = offset;
+    p.kv_head_stride = static_cast<int64_t>(cap) * kHeadDim;
+    p.G = G;
+    p.cap = cap;
+    p.T = T;
+    p.H = H;
+    p.R = R;
+    p.nunits = nunits;
+    p.hw = -1;
+    p.causal = 1;
+    p.scale = scale;
+    if (cos != nullptr) launch_shape<2, false>(sh, p, grid, stream);
+    else launch_shape<0, false>(sh, p, grid, stream);
+    return check_launch(fn);
 }

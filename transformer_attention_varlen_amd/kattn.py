@@ -24,7 +24,8 @@ KATTN_EDEVICE = -4
 
 EXPORTS = ("kattn_last_error", "kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
            "kattn_varlen_fwd_workspace", "kattn_varlen_fwd", "kattn_varlen_fwd_rope",
-           "kattn_varlen_fwd_f16", "kattn_decode_workspace", "kattn_decode")
+           "kattn_varlen_fwd_f16", "kattn_prefill_cached_workspace", "kattn_prefill_cached",
+           "kattn_decode_workspace", "kattn_decode")
 
 
 class KattnError(RuntimeError):
@@ -59,13 +60,17 @@ def lib():
                    p, p, i32, p, sz, p]
         L.kattn_varlen_fwd_rope.argtypes = fwd_tab
         L.kattn_varlen_fwd_f16.argtypes = fwd_tab
+        L.kattn_prefill_cached_workspace.argtypes = [i32, i32]
+        L.kattn_prefill_cached_workspace.restype = sz
+        L.kattn_prefill_cached.argtypes = [p, i64, p, i64, p, i64, p, i64, p, p, i32, i32, i32, i32,
+                                           p, p, i32, i32, i32, i32, f32, p, p, i32, p, sz, p]
         L.kattn_decode_workspace.argtypes = [i32, i32, i32]
         L.kattn_decode_workspace.restype = sz
         L.kattn_decode.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, f32, p, p,
                                    i32, p, sz, p]
         for name in ("kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
                      "kattn_varlen_fwd", "kattn_varlen_fwd_rope", "kattn_varlen_fwd_f16",
-                     "kattn_decode"):
+                     "kattn_prefill_cached", "kattn_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,6 +177,24 @@ def kattn_varlen_fwd_f16(out, q, k, v, cu, S: int, T: int, max_seqlen: int, H: i
                                       H, G, HEAD_DIM, int(window), int(bool(causal)),
                                       float(scale), _dev(cos), _dev(sin), table_len,
                                       _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def kattn_prefill_cached_workspace(B: int, T: int) -> int:
+    return int(lib().kattn_prefill_cached_workspace(int(B), int(T)))
+
+
+def kattn_prefill_cached(out, q, k_new, v_new, cu, offset, B: int, T: int, max_chunk: int,
+                         max_ctx: int, k_cache, v_cache, cap: int, H: int, G: int, *,
+                         scale: float = 0.125, cos=None, sin=None, workspace=None, stream=None):
+    """Chunked prefill continuing from the caches; the chunk is appended at rows offset[b].."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    table_len = 0 if cos is None else int(cos.shape[0])
+    _check(lib().kattn_prefill_cached(_dev(out), _stride(out), _dev(q), _stride(q), _dev(k_new),
+                                      _stride(k_new), _dev(v_new), _stride(v_new), _dev(cu),
+                                      _dev(offset), B, T, max_chunk, max_ctx, _dev(k_cache),
+                                      _dev(v_cache), cap, H, G, HEAD_DIM, float(scale), _dev(cos),
+                                      _dev(sin), table_len, _dev(workspace), ws_bytes,
+                                      _stream(stream)))
 
 
 def kattn_decode(out, q, k_new, v_new, k_cache, v_cache, cap: int, used, max_used: int, B: int,

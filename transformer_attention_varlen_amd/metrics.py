@@ -42,6 +42,18 @@ def prefill_flops(lengths, H: int, window: int = -1, causal: bool = False) -> in
     return FLOPS_PER_PAIR * H * visible_pairs_per_head(lengths, window, causal)
 
 
+def chunk_pairs_per_head(lengths, offsets) -> int:
+    """Visible (query, key) pairs of chunks continuing from a cache: row i of a chunk whose
+    sequence already holds `off` rows sees keys 0 .. off + i."""
+    n = np.asarray(lengths, dtype=np.int64)
+    o = np.asarray(offsets, dtype=np.int64)
+    return int(np.sum(n * o + n * (n + 1) // 2))
+
+
+def chunk_flops(lengths, offsets, H: int) -> int:
+    return FLOPS_PER_PAIR * H * chunk_pairs_per_head(lengths, offsets)
+
+
 def prefill_bytes(T: int, H: int, G: int) -> int:
     """q, k, v read and out written, f32."""
     return T * (H + 2 * G) * HEAD_DIM * F32 + T * H * HEAD_DIM * F32

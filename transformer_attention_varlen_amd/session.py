@@ -6,6 +6,8 @@ This is call sequencing only -- every step of the path runs in libkattn.so:
             (in place on q and k) -> kattn_varlen_fwd; or, fused, kattn_varlen_fwd_rope
             (q and k read-only, rotated inside the tile loads)
   decode:   kattn_decode (rotate + append + split-K + combine)
+  chunk:    kattn_prefill_cached (append the chunk at the fill point, then its queries
+            against the cache rows up to their positions)
 
 Inputs are copied to HBM once when a run is created; ``step()`` then touches
 only device memory, so a timed loop over ``step()`` measures the kernels with
@@ -17,7 +19,7 @@ import numpy as np
 import torch
 
 from . import kattn
-from .workloads import DecodeCase, PrefillCase
+from .workloads import ChunkCase, DecodeCase, PrefillCase
 
 HEAD_DIM = 64
 
@@ -135,3 +137,36 @@ class DecodeRun:
         kattn.kattn_decode(self.out, self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
                            c.cap, self.used, self.max_used, c.B, c.H, c.G, scale=0.125,
                            cos=self.cos, sin=self.sin, workspace=self.workspace)
+
+
+class ChunkRun:
+    """Device buffers for a ChunkCase and the call of one chunked-prefill step."""
+
+    def __init__(self, case: ChunkCase, device="cuda", rotate: bool = True, out_pad_rows: int = 0):
+        self.case = case
+        self.k_cache = _to_dev(case.k_cache, device)
+        self.v_cache = _to_dev(case.v_cache, device)
+        self.q = _to_dev(case.q, device)
+        self.k = _to_dev(case.k, device)
+        self.v = _to_dev(case.v, device)
+        self.cu = _to_dev(case.cu, device)
+        self.offsets = _to_dev(case.offsets, device)
+        if rotate:
+            self.cos_h, self.sin_h = kattn.kattn_rope_tables(case.theta, case.cap)
+            self.cos = _to_dev(self.cos_h, device)
+            self.sin = _to_dev(self.sin_h, device)
+        else:
+            self.cos = self.sin = None
+        T = case.T
+        self.out_full = torch.empty((T + out_pad_rows, case.H * HEAD_DIM), dtype=torch.float32,
+                                    device=device)
+        self.out = self.out_full[:T]
+        ws = kattn.kattn_prefill_cached_workspace(case.B, T)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    def step(self):
+        c = self.case
+        kattn.kattn_prefill_cached(self.out, self.q, self.k, self.v, self.cu, self.offsets, c.B,
+                                   c.T, c.max_chunk, c.max_ctx, self.k_cache, self.v_cache, c.cap,
+                                   c.H, c.G, scale=0.125, cos=self.cos, sin=self.sin,
+                                   workspace=self.workspace)

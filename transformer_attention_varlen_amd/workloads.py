@@ -6,7 +6,8 @@ arrays it returns.
 
 Recipe (one ``numpy.random.default_rng(seed)`` PCG64 stream per case; draw
 order: sequence lengths, then the activations, then -- for decode -- the
-caches K, V, the new q, k, v and the used lengths):
+caches K, V, the new q, k, v and the used lengths; for a chunked prefill: the
+chunk lengths, the filled rows (offsets), then the caches K, V, then q, k, v):
 
 * values are ``standard_normal(dtype=float32)``, i.e. N(0, 1);
 * a packed layout draws one (T, (H + 2G) * 64) array whose columns are the q
@@ -78,6 +79,41 @@ class DecodeCase:
         return int(self.used.max()) if self.B else 0
 
 
+@dataclass
+class ChunkCase:
+    """Prefill of one chunk per sequence continuing from filled KV caches."""
+    name: str
+    lengths: np.ndarray        # int32 [B], rows of each chunk
+    cu: np.ndarray             # int32 [B+1]
+    offsets: np.ndarray        # int32 [B], cache rows filled before the chunk
+    H: int
+    G: int
+    cap: int
+    theta: float
+    k_cache: np.ndarray        # (B, G, cap, 64) float32
+    v_cache: np.ndarray
+    q: np.ndarray              # (T, H*64)
+    k: np.ndarray              # (T, G*64)
+    v: np.ndarray              # (T, G*64)
+    seed: int = 0
+
+    @property
+    def B(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def T(self) -> int:
+        return int(self.cu[-1])
+
+    @property
+    def max_chunk(self) -> int:
+        return int(self.lengths.max()) if self.B else 0
+
+    @property
+    def max_ctx(self) -> int:
+        return int((self.offsets + self.lengths).max()) if self.B else 0
+
+
 def _cu(lengths: np.ndarray) -> np.ndarray:
     cu = np.zeros(lengths.shape[0] + 1, np.int32)
     np.cumsum(lengths, out=cu[1:])
@@ -117,6 +153,25 @@ def make_decode(B: int, H: int, G: int, cap: int, used_lo: int, used_hi: int, *,
     return DecodeCase(name, B, H, G, cap, theta, k_cache, v_cache, q_new, k_new, v_new, used, seed)
 
 
+def make_chunked(lengths, offsets, H: int, G: int, cap: int, *, theta: float = 100000.0,
+                 seed: int = 0, rng: np.random.Generator | None = None,
+                 name: str = "custom") -> ChunkCase:
+    """Filled caches and one chunk of new rows per sequence."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    lengths = np.asarray(lengths, dtype=np.int32)
+    offsets = np.asarray(offsets, dtype=np.int32)
+    B = lengths.shape[0]
+    cu = _cu(lengths)
+    T = int(cu[-1])
+    k_cache = rng.standard_normal((B, G, cap, HEAD_DIM), dtype=np.float32)
+    v_cache = rng.standard_normal((B, G, cap, HEAD_DIM), dtype=np.float32)
+    q = rng.standard_normal((T, H * HEAD_DIM), dtype=np.float32)
+    k = rng.standard_normal((T, G * HEAD_DIM), dtype=np.float32)
+    v = rng.standard_normal((T, G * HEAD_DIM), dtype=np.float32)
+    return ChunkCase(name, lengths, cu, offsets, H, G, cap, theta, k_cache, v_cache, q, k, v,
+                     seed)
+
+
 # --- the named workloads -------------------------------------------------------------
 
 @dataclass(frozen=True)
@@ -124,7 +179,7 @@ class Workload:
     key: str
     name: str
     seed: int
-    kind: str                 # "prefill" | "decode"
+    kind: str                 # "prefill" | "decode" | "chunk"
     desc: str
     params: dict = field(default_factory=dict)
 
@@ -158,6 +213,12 @@ WORKLOADS = {
                   "64 sequences, one new token each, 9 q heads / 3 kv heads, caches "
                   "[64][3][8192][64] f32, used U[1143,8192], theta 1e5",
                   dict(B=64, H=9, G=3, cap=8192, used_range=(1143, 8192), theta=100000.0)),
+    "5": Workload("5", "smollm2_chunked_prefill_b16", 1005, "chunk",
+                  "16 sequences continuing from filled caches [16][3][8192][64] f32: chunks of "
+                  "U[128,1024] new rows after U[0,4096] filled rows, 9 q heads / 3 kv heads, "
+                  "theta 1e5",
+                  dict(B=16, H=9, G=3, cap=8192, len_range=(128, 1024), off_range=(0, 4096),
+                       theta=100000.0)),
 }
 
 
@@ -170,6 +231,11 @@ def build(key: str):
         return make_decode(p["B"], p["H"], p["G"], p["cap"], lo, hi, theta=p["theta"],
                            seed=w.seed, name=w.name)
     rng = np.random.default_rng(w.seed)
+    if w.kind == "chunk":
+        lengths = rng.integers(*p["len_range"], size=p["B"], endpoint=True).astype(np.int32)
+        offsets = rng.integers(*p["off_range"], size=p["B"], endpoint=True).astype(np.int32)
+        return make_chunked(lengths, offsets, p["H"], p["G"], p["cap"], theta=p["theta"],
+                            rng=rng, name=w.name, seed=w.seed)
     if "lengths" in p:
         lengths = np.asarray(p["lengths"], np.int32)
     else:
