@@ -133,11 +133,18 @@ def decode_part(torch, steps, warmup, flush):
     case = wl.build("4")
     run = DecodeRun(case, rotate=True)
     mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
+    # the same step captured once in a HIP graph and replayed (fixed shape, device counts)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run.step()
+    graph_ms, _ = time_calls(torch, graph.replay, steps, warmup, flush)
+    del graph
     nbytes = metrics.decode_bytes(case.used, case.H, case.G)
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     res = {"workload": wl.WORKLOADS["4"].name, "seqs": case.B, "heads": case.H,
            "kv_heads": case.G, "cap": case.cap, "sum_used": int(case.used.sum()),
            "decode_ms": round(mean_ms, 4), "decode_ms_min": round(min_ms, 4),
+           "graph_replay_ms": round(graph_ms, 4),
            "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     del run
@@ -317,6 +324,19 @@ def main():
         run.step()
     torch.cuda.synchronize()
     two_pass_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    # the fused step captured once in a HIP graph and replayed back to back
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run.step_fused()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    del graph
     flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     value = case.T / (ms_per_step * 1e-3) / 1e6
@@ -331,7 +351,8 @@ def main():
                    "causal": case.causal, "rope_theta": case.theta,
                    "seed": wl.WORKLOADS[HEADLINE].seed,
                    "step": "attention forward with RoPE fused into the tile loads",
-                   "two_pass_ms_per_step": round(two_pass_ms, 4)},
+                   "two_pass_ms_per_step": round(two_pass_ms, 4),
+                   "graph_replay_ms_per_step": round(graph_ms, 4)},
         "roofline": {"bound": "mfma",
                      "kernel": "fwd_kernel, fused-RoPE variant (events span the planner too)",
                      "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,

@@ -33,6 +33,24 @@
  *   environment each call copies its device tables to the host, validates
  *   them and returns KATTN_EBOUNDS on a bad one (synchronous; debugging
  *   only).
+ *
+ * Fixed shapes and graph capture
+ * ------------------------------
+ * The work of every device call is scheduled on the device from the device
+ * tables (the query-tile list from cu, the decode key split from used), so a
+ * launch's shape depends only on the host sizes.  A caller that captures a
+ * fixed shape (a HIP graph, the pages' remark that padding matters to a
+ * backend capturing one shape) sizes the call for a bucket and writes the
+ * real counts into the device tables before each replay:
+ *   - prefill (kattn_varlen_fwd*, kattn_prefill_cached): S and T are the
+ *     bucket's; cu may end below T (cu[S] <= T) and trailing sequences may be
+ *     empty.  Rows at and past cu[S] are neither read nor written.
+ *     max_seqlen (max_chunk, max_ctx) is the bucket's bound.
+ *   - decode: B is the bucket's; a slot with used[b] = 0 is skipped (its out
+ *     row and caches untouched).  max_used is the bound (cap, say).
+ * No call allocates, synchronises or queues a memset or a copy, so each can
+ * be captured on the caller's stream (not with KATTN_CHECK=1).  A captured
+ * call keeps the pointers and host sizes it was captured with.
  */
 #ifndef KATTN_H
 #define KATTN_H
@@ -124,7 +142,8 @@ size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T);
  *               and columns >= H*64 are never written.
  *   q, k, v:    device float (T, H*64), (T, G*64), (T, G*64) with their own
  *               strides (a packed qkv row: k = q + H*64, v = k + G*64).
- *   cu:         device int32[S+1], the offsets of kattn_build_index.
+ *   cu:         device int32[S+1], the offsets of kattn_build_index, or a
+ *               bucket's padded offsets with cu[S] <= T (see above).
  *   max_seqlen: longest sequence (host scalar, from kattn_build_index).  It must not
  *               be smaller than the longest sequence: a window whose half-width reaches
  *               max_seqlen - 1 masks nothing and runs as global attention.
