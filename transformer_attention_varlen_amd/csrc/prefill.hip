@@ -242,17 +242,208 @@ __device__ inline float ror8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
+// One tile's online-softmax update for the 32 queries of a wave (column j of lane j and
+// j + 32): S^T = K Q^T on FP32 MFMA from the staged K rows, the boundary mask when the tile
+// is not fully visible (masked scores become -inf, the same as skipping them), the running
+// max and sum, and O^T += V^T P^T from the staged V rows.  TWO: a 64-key tile (two 32-key
+// score blocks).
+template <bool TWO>
+__device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
+                                            const float (&qreg)[32], f32x16& O0, f32x16& O1,
+                                            float& m_run, float& l_run, bool full, int kt,
+                                            int nk, int pq, int causal, int hw, int j, int hh) {
+    // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
+    f32x16 S0, S1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        S0[r] = 0.0f;
+        S1[r] = 0.0f;
+    }
+    const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
+    const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
+        S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
+        S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
+        S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
+        S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
+        if constexpr (TWO) {
+            const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
+        }
+    }
+
+    if (!full) {
+        // boundary tile: masked scores become -inf (the same as skipping them)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int key1 = key0 + 32;
+            bool v0 = key0 < nk, v1 = key1 < nk;
+            if (causal) {
+                v0 = v0 && key0 <= pq;
+                v1 = v1 && key1 <= pq;
+            }
+            if (hw >= 0) {
+                v0 = v0 && abs(pq - key0) <= hw;
+                v1 = v1 && abs(pq - key1) <= hw;
+            }
+            if (!v0) S0[r] = -INFINITY;
+            if (TWO && !v1) S1[r] = -INFINITY;
+        }
+    }
+
+    // online softmax
+    float mx = S0[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+    if constexpr (TWO) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+    const float ml = m_new * kLog2e;
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
+        psum += S0[r];
+        if constexpr (TWO) {
+            S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
+            psum += S1[r];
+        }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        O0[r] *= alpha;
+        O1[r] *= alpha;
+    }
+
+    // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
+        O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
+        O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
+        if constexpr (TWO) {
+            const float2 vb =
+                *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
+            O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
+            O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
+        }
+    }
+}
+
 // TBN: keys per K/V tile.  Global launches use 64-key tiles (two 32-key score blocks per MFMA
 // round, fewer barriers per flop).  Banded launches (a window or a causal limit) use 32-key
 // tiles: a wave's band is covered with less waste, and half the score and staging registers
-// leave room for a third wave per SIMD.
+// leave room for a fourth wave per SIMD.
 // ROT: 0, q and k arrive rotated; 1, q and k arrive unrotated: q is rotated as it is loaded
 // and every K row as it is staged in LDS, at its position inside the sequence (the RoPE step
 // of kime-cpu plan.rs `Ctx::step` and argus text.rs `rope`, moved into the tile loads); 2,
 // only q is rotated (keys come from a cache that holds rotated rows).
 // F16: the output is written as IEEE binary16 (round to nearest even) instead of FP32.
+// The Q slice of one lane: dims 32hh .. 32hh+31 of the query in packed row `row` at
+// position pq, times scale; rotated at pq first when ROT != 0; zeros when !live.
+template <int ROT>
+__device__ __forceinline__ void load_q(float (&qreg)[32], const FwdParams& p, int64_t row,
+                                       int head, int pq, int hh, bool live) {
+    if (live) {
+        const float* qrow = p.q + row * p.q_stride + head * kHeadDim;
+        const float4* src = reinterpret_cast<const float4*>(qrow + hh * 32);
+        if constexpr (ROT != 0) {
+            // pairs (x[i], x[i+32]) at position pq: the low lane half loads dims 0..31 and the
+            // cos row, the high half dims 32..63 and the sin row; a permlane32 swap then gives
+            // every lane both members of each pair and both tables (low value first).
+            const int64_t prow = min(pq, p.table_len - 1);
+            const float4* tq = reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
+            float4 xa[8], ta[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                xa[m] = src[m];
+                ta[m] = tq[m];
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+                const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
+                                                                     __float_as_uint(xs[c]), false, false);
+                    const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
+                                                                     __float_as_uint(ts[c]), false, false);
+                    const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
+                    const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
+                    const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
+                    qreg[4 * m + c] = r * p.scale;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 t = src[m];
+                qreg[4 * m + 0] = t.x * p.scale;
+                qreg[4 * m + 1] = t.y * p.scale;
+                qreg[4 * m + 2] = t.z * p.scale;
+                qreg[4 * m + 3] = t.w * p.scale;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
+    }
+
+}
+
+// Orders one wave's LDS accesses between its own lanes (a wave never shares its region).
+__device__ inline void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Eight consecutive output values (a then b) at element offset `at`: two 16-byte FP32
+// stores, or with F16 one 16-byte store of eight binary16 values (round to nearest even).
+template <bool F16>
+__device__ __forceinline__ void store8(void* out, int64_t at, float4 a, float4 b) {
+    if constexpr (F16) {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        h8 hv;
+        hv[0] = static_cast<_Float16>(a.x);
+        hv[1] = static_cast<_Float16>(a.y);
+        hv[2] = static_cast<_Float16>(a.z);
+        hv[3] = static_cast<_Float16>(a.w);
+        hv[4] = static_cast<_Float16>(b.x);
+        hv[5] = static_cast<_Float16>(b.y);
+        hv[6] = static_cast<_Float16>(b.z);
+        hv[7] = static_cast<_Float16>(b.w);
+        *reinterpret_cast<h8*>(static_cast<_Float16*>(out) + at) = hv;
+    } else {
+        float* dst = static_cast<float*>(out) + at;
+        *reinterpret_cast<float4*>(dst) = a;
+        *reinterpret_cast<float4*>(dst + 4) = b;
+    }
+}
+
+// Waves per SIMD the register budget targets: measured best without spills (the K rotation
+// of ROT = 1 needs the extra registers of one wave fewer).
+template <int TBN, int ROT>
+constexpr int fwd_waves() {
+    return ROT == 1 ? (TBN == 32 ? 3 : 2) : (TBN == 32 ? 4 : 3);
+}
+
 template <int HPW, int QW, int TBN, int ROT, bool F16>
-__global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(TBN == 32 ? 3 : 2)))
+__global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(fwd_waves<TBN, ROT>())))
 void fwd_kernel(FwdParams p) {
     static_assert(TBN == 32 || TBN == 64, "tiles hold one or two 32-key score blocks");
     constexpr bool ROPE_Q = ROT != 0, ROPE_K = ROT == 1;
@@ -386,51 +577,7 @@ void fwd_kernel(FwdParams p) {
 
     // Q slice: dims 32hh .. 32hh+31 of query qi, times scale.
     float qreg[32];
-    if (qi < n) {
-        const float* qrow = p.q + static_cast<int64_t>(lo + qi) * p.q_stride + head * kHeadDim;
-        const float4* src = reinterpret_cast<const float4*>(qrow + hh * 32);
-        if constexpr (ROPE_Q) {
-            // pairs (x[i], x[i+32]) at position pq: the low lane half loads dims 0..31 and the
-            // cos row, the high half dims 32..63 and the sin row; a permlane32 swap then gives
-            // every lane both members of each pair and both tables (low value first).
-            const int64_t prow = min(pq, p.table_len - 1);
-            const float4* tq = reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
-            float4 xa[8], ta[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                xa[m] = src[m];
-                ta[m] = tq[m];
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
-                const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
-                                                                     __float_as_uint(xs[c]), false, false);
-                    const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
-                                                                     __float_as_uint(ts[c]), false, false);
-                    const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
-                    const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
-                    const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
-                    qreg[4 * m + c] = r * p.scale;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 t = src[m];
-                qreg[4 * m + 0] = t.x * p.scale;
-                qreg[4 * m + 1] = t.y * p.scale;
-                qreg[4 * m + 2] = t.z * p.scale;
-                qreg[4 * m + 3] = t.w * p.scale;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
-    }
+    load_q<ROT>(qreg, p, static_cast<int64_t>(lo + qi), head, pq, hh, qi < n);
 
     KATTN_STASH()
     __syncthreads();
@@ -450,97 +597,9 @@ void fwd_kernel(FwdParams p) {
             any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
-        if (any) {
-            // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
-            f32x16 S0, S1;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                S0[r] = 0.0f;
-                S1[r] = 0.0f;
-            }
-            const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
-            const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
-                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
-                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
-                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
-                S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
-                if constexpr (TWO) {
-                    const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
-                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
-                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
-                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
-                    S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
-                }
-            }
-
-            if (!full) {
-                // boundary tile: masked scores become -inf (the same as skipping them)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    const int key1 = key0 + 32;
-                    bool v0 = key0 < nk, v1 = key1 < nk;
-                    if (p.causal) {
-                        v0 = v0 && key0 <= pq;
-                        v1 = v1 && key1 <= pq;
-                    }
-                    if (p.hw >= 0) {
-                        v0 = v0 && abs(pq - key0) <= p.hw;
-                        v1 = v1 && abs(pq - key1) <= p.hw;
-                    }
-                    if (!v0) S0[r] = -INFINITY;
-                    if (TWO && !v1) S1[r] = -INFINITY;
-                }
-            }
-
-            // online softmax
-            float mx = S0[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
-            if constexpr (TWO) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-            const float ml = m_new * kLog2e;
-            m_run = m_new;
-            float psum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
-                psum += S0[r];
-                if constexpr (TWO) {
-                    S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
-                    psum += S1[r];
-                }
-            }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                O0[r] *= alpha;
-                O1[r] *= alpha;
-            }
-
-            // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key0 = 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float2 va = *reinterpret_cast<const float2*>(&Vs[key0 * LDS_STRIDE + 2 * j]);
-                O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, S0[r], O0, 0, 0, 0);
-                O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, S0[r], O1, 0, 0, 0);
-                if constexpr (TWO) {
-                    const float2 vb =
-                        *reinterpret_cast<const float2*>(&Vs[(key0 + 32) * LDS_STRIDE + 2 * j]);
-                    O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.x, S1[r], O0, 0, 0, 0);
-                    O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
-                }
-            }
-        }
+        if (any)
+            tile_update<TWO>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, nk, pq, p.causal, p.hw, j,
+                             hh);
 
         __syncthreads();  // every wave is done with this tile
         if (kt + TBN < kend) KATTN_STASH()
@@ -568,26 +627,176 @@ void fwd_kernel(FwdParams p) {
             b.y = O1[r0 + 2] * inv;
             b.z = O0[r0 + 3] * inv;
             b.w = O1[r0 + 3] * inv;
-            if constexpr (F16) {
-                // dims 2*i0 .. 2*i0+7 as eight halves: one 16-byte store
-                typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-                h8 hv;
-                hv[0] = static_cast<_Float16>(a.x);
-                hv[1] = static_cast<_Float16>(a.y);
-                hv[2] = static_cast<_Float16>(a.z);
-                hv[3] = static_cast<_Float16>(a.w);
-                hv[4] = static_cast<_Float16>(b.x);
-                hv[5] = static_cast<_Float16>(b.y);
-                hv[6] = static_cast<_Float16>(b.z);
-                hv[7] = static_cast<_Float16>(b.w);
-                *reinterpret_cast<h8*>(static_cast<_Float16*>(p.out) + at + 2 * i0) = hv;
-            } else {
-                float* dst = static_cast<float*>(p.out) + at;
-                *reinterpret_cast<float4*>(dst + 2 * i0) = a;
-                *reinterpret_cast<float4*>(dst + 2 * i0 + 4) = b;
-            }
+            store8<F16>(p.out, at + 2 * i0, a, b);
         }
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Key-split variant for launches whose query tiles are too few to fill the GPU (one long
+// causal sequence, say): the 4 waves of a work-group take the same 32 queries of one head and
+// split the block's key tiles four ways.  Each wave stages its own 32-key tiles in its own LDS
+// region (wave-level synchronisation only), and the four partial results are merged through
+// LDS at the end with the log-sum-exp algebra: M = max m_w, l = sum l_w e^(m_w - M),
+// O = sum O_w e^(m_w - M) / l, wave w writing dims 16w .. 16w+15.  The per-tile math is the
+// main kernel's (tile_update).
+constexpr int kSplitWaves = 4;
+constexpr int kSplitTBN = 32;
+
+template <int ROT, bool F16>
+__global__ __launch_bounds__(64 * kSplitWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_split_kernel(FwdParams p) {
+    constexpr int TBN = kSplitTBN;
+    constexpr bool ROPE_K = ROT == 1;
+    // per wave: K rows then V rows of its current tile; after the loop, its partial result
+    __shared__ __attribute__((aligned(16))) float lds[kSplitWaves][2 * TBN * LDS_STRIDE];
+    static_assert(34 * 64 <= 2 * TBN * LDS_STRIDE, "a wave's partial result fits its region");
+
+    const int tix = blockIdx.x / p.nunits;
+    const int head = blockIdx.x - tix * p.nunits;
+    if (tix >= *p.count) return;
+    const int2 tile = p.tiles[tix];
+    const SeqRange sr = seq_range(p.cu, tile.x, p.T);
+    const int lo = sr.lo, n = sr.n, q0 = tile.y;
+    int off, nk;
+    key_count(p.kv_off, p.cap, tile.x, n, off, nk);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 31, hh = lane >> 5;
+    const int g = head / p.R;
+    const int qi = q0 + j;
+    const int qlast_w = min(q0 + 31, n - 1);
+    const int pa = off + q0, plast_w = off + qlast_w, pq = off + qi;
+
+    int kbeg, kend;
+    key_range(pa, off + min(q0 + 32, n), nk, p.hw, p.causal, kbeg, kend);
+    kbeg = (kbeg / TBN) * TBN;
+    const int ntiles = kend > kbeg ? (kend - kbeg + TBN - 1) / TBN : 0;
+    const int t0 = kbeg + (wave * ntiles / kSplitWaves) * TBN;            // this wave's tiles
+    const int t1 = min(kend, kbeg + ((wave + 1) * ntiles / kSplitWaves) * TBN);
+
+    const float* kbase;
+    const float* vbase;
+    if (p.kv_off != nullptr) {
+        const int64_t h0 = (static_cast<int64_t>(tile.x) * p.G + g) * p.kv_head_stride;
+        kbase = p.k + h0;
+        vbase = p.v + h0;
+    } else {
+        kbase = p.k + static_cast<int64_t>(lo) * p.k_stride + g * kHeadDim;
+        vbase = p.v + static_cast<int64_t>(lo) * p.v_stride + g * kHeadDim;
+    }
+    float* Ks = lds[wave];
+    float* Vs = lds[wave] + TBN * LDS_STRIDE;
+
+    // staging: 16 lanes per row, rows lrow + 4i of the tile.  Native 4-float vectors: copies of
+    // the HIP vector struct would go through private memory.
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const int lrow = lane >> 4, lcol = lane & 15;
+    constexpr int kPieces = TBN / 4;
+    v4 pk[kPieces], pv[kPieces], pt[kPieces];
+    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+#define KATTN_SPLIT_FETCH(K0)                                                                    \
+    _Pragma("unroll") for (int i = 0; i < kPieces; ++i) {                                        \
+        const int64_t r = min((K0) + lrow + 4 * i, nk - 1);                                      \
+        pk[i] = reinterpret_cast<const v4*>(kbase + r * p.k_stride)[lcol];                       \
+        pv[i] = reinterpret_cast<const v4*>(vbase + r * p.v_stride)[lcol];                       \
+        if constexpr (ROPE_K)                                                                    \
+            pt[i] = reinterpret_cast<const v4*>(                                                 \
+                tab + min(r, static_cast<int64_t>(p.table_len) - 1) * 32)[0];                    \
+    }
+#define KATTN_SPLIT_STASH()                                                                      \
+    _Pragma("unroll") for (int i = 0; i < kPieces; ++i) {                                        \
+        v4 x = pk[i];                                                                            \
+        if constexpr (ROPE_K) {                                                                  \
+            const v4 tt = pt[i];                                                                 \
+            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                           \
+            const v4 u = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                       \
+            x = lcol < 8 ? x * tt - y * u : x * u + y * tt;                                      \
+        }                                                                                        \
+        *reinterpret_cast<v4*>(&Ks[(lrow + 4 * i) * LDS_STRIDE + 4 * lcol]) = x;                 \
+        *reinterpret_cast<v4*>(&Vs[(lrow + 4 * i) * LDS_STRIDE + 4 * lcol]) = pv[i];             \
+    }
+
+    if (t0 < t1) {
+        KATTN_SPLIT_FETCH(t0)
+    }
+    float qreg[32];
+    load_q<ROT>(qreg, p, static_cast<int64_t>(lo + qi), head, pq, hh, qi < n);
+    f32x16 O0, O1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        O0[r] = 0.0f;
+        O1[r] = 0.0f;
+    }
+    float m_run = kNegBig, l_run = 0.0f;
+    if (t0 < t1) {
+        KATTN_SPLIT_STASH()
+        wave_sync_lds();
+    }
+    for (int kt = t0; kt < t1; kt += TBN) {
+        if (kt + TBN < t1) {  // the next tile's rows fly during this tile's math
+            KATTN_SPLIT_FETCH(kt + TBN)
+        }
+        const int klast = kt + TBN - 1;
+        bool any = kt < nk, full = klast < nk;
+        if (p.causal) {
+            any = any && kt <= plast_w;
+            full = full && klast <= pa;
+        }
+        if (p.hw >= 0) {
+            any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
+            full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
+        }
+        if (any)
+            tile_update<false>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, nk, pq, p.causal,
+                               p.hw, j, hh);
+        wave_sync_lds();  // this wave is done with the tile
+        if (kt + TBN < t1) {
+            KATTN_SPLIT_STASH()
+            wave_sync_lds();
+        }
+    }
+#undef KATTN_SPLIT_FETCH
+#undef KATTN_SPLIT_STASH
+
+    // merge the four partial results through LDS
+    __syncthreads();  // every wave is done with its staging region
+    float* mine = lds[wave];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        mine[r * 64 + lane] = O0[r];
+        mine[(16 + r) * 64 + lane] = O1[r];
+    }
+    mine[32 * 64 + lane] = m_run;
+    mine[33 * 64 + lane] = l_run;
+    __syncthreads();
+    if (qi >= n) return;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, lds[w][32 * 64 + lane]);
+    float l_tot = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    const int r0 = 4 * wave;  // this wave writes result rows r0 .. r0+3 of O0 and O1
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+        const float* part = lds[w];
+        const float f = __builtin_amdgcn_exp2f((part[32 * 64 + lane] - M) * kLog2e);
+        l_tot = __builtin_fmaf(part[33 * 64 + lane] + part[33 * 64 + (lane ^ 32)], f, l_tot);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[2 * k] = __builtin_fmaf(part[(r0 + k) * 64 + lane], f, acc[2 * k]);
+            acc[2 * k + 1] = __builtin_fmaf(part[(16 + r0 + k) * 64 + lane], f, acc[2 * k + 1]);
+        }
+    }
+    const float inv = 1.0f / l_tot;
+    const int i0 = 8 * wave + 4 * hh;  // result rows i0..i0+3 -> dims 2*i0 .. 2*i0+7
+    const float4 a = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    const float4 b = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    store8<F16>(p.out, static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim + 2 * i0, a,
+                b);
 }
 
 // Work-group shape per q-heads-per-kv-head ratio R: HPW heads x QW query blocks.
@@ -612,6 +821,39 @@ void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
     else if constexpr (ROT != 2)  // keys from a cache are always causal
         hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64, ROT, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
+}
+
+// Launches with fewer work-groups than this (a quarter of the 4-wave slots of 256 CUs at 2
+// work-groups each) use the key-split kernel instead: four times the waves, each over a
+// quarter of the keys.
+constexpr int64_t kSplitBelow = 512;
+
+template <int ROT, bool F16>
+void launch_split(const FwdParams& p, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_split_kernel<ROT, F16>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * kSplitWaves), 0, stream, p);
+}
+
+// The launch geometry of a forward call: query block rows, work-groups per query block and
+// whether the key-split kernel runs.
+struct Geometry {
+    int BM, nunits;
+    int64_t capacity, grid;
+    bool split;
+};
+Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
+    Geometry gm;
+    gm.BM = 32 * sh.qw;
+    gm.nunits = H / sh.hpw;
+    gm.capacity = tile_capacity(S, T, gm.BM);
+    gm.split = gm.capacity * gm.nunits < kSplitBelow;
+    if (gm.split) {  // 32-row query blocks, one head per work-group
+        gm.BM = 32;
+        gm.nunits = H;
+        gm.capacity = tile_capacity(S, T, 32);
+    }
+    gm.grid = gm.capacity * gm.nunits;
+    return gm;
 }
 
 template <int ROT, bool F16>
@@ -734,10 +976,11 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
 
     const int R = H / G;
     const Shape sh = pick_shape(R);
-    const int BM = 32 * sh.qw;
-    const int64_t capacity = tile_capacity(S, T, BM);
-    const int nunits = H / sh.hpw;
-    const int64_t grid = capacity * nunits;
+    const Geometry gm = fwd_geometry(S, T, H, sh);
+    const int BM = gm.BM;
+    const int64_t capacity = gm.capacity;
+    const int nunits = gm.nunits;
+    const int64_t grid = gm.grid;
     if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
     // Half window.  A window that reaches across the longest sequence masks nothing, so it
     // runs as global attention (the same kernel and the same bits as window = -1).
@@ -779,7 +1022,12 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.hw = hw;
     p.causal = causal;
     p.scale = scale;
-    if (rope && out_f16) launch_shape<1, true>(sh, p, grid, stream);
+    if (gm.split) {
+        if (rope && out_f16) launch_split<1, true>(p, grid, stream);
+        else if (rope) launch_split<1, false>(p, grid, stream);
+        else if (out_f16) launch_split<0, true>(p, grid, stream);
+        else launch_split<0, false>(p, grid, stream);
+    } else if (rope && out_f16) launch_shape<1, true>(sh, p, grid, stream);
     else if (rope) launch_shape<1, false>(sh, p, grid, stream);
     else if (out_f16) launch_shape<0, true>(sh, p, grid, stream);
     else launch_shape<0, false>(sh, p, grid, stream);
@@ -904,10 +1152,11 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     // 2. the chunk's queries against cache rows 0 .. offset + i (causal with an offset)
     const int R = H / G;
     const Shape sh = pick_shape(R);
-    const int BM = 32 * sh.qw;
-    const int64_t capacity = tile_capacity(B, T, BM);
-    const int nunits = H / sh.hpw;
-    const int64_t grid = capacity * nunits;
+    const Geometry gm = fwd_geometry(B, T, H, sh);
+    const int BM = gm.BM;
+    const int64_t capacity = gm.capacity;
+    const int nunits = gm.nunits;
+    const int64_t grid = gm.grid;
     if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
     char* ws = static_cast<char*>(workspace);
     int32_t* count = reinterpret_cast<int32_t*>(ws);
@@ -944,7 +1193,10 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     p.hw = -1;
     p.causal = 1;
     p.scale = scale;
-    if (cos != nullptr) launch_shape<2, false>(sh, p, grid, stream);
+    if (gm.split) {
+        if (cos != nullptr) launch_split<2, false>(p, grid, stream);
+        else launch_split<0, false>(p, grid, stream);
+    } else if (cos != nullptr) launch_shape<2, false>(sh, p, grid, stream);
     else launch_shape<0, false>(sh, p, grid, stream);
     return check_launch(fn);
 }
