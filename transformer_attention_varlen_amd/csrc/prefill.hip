@@ -463,7 +463,7 @@ void fwd_kernel(FwdParams p) {
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // uniform per wave
     const int j = lane & 31;   // query column of this lane
     const int hh = lane >> 5;  // lane half
     const int head = unit * HPW + (wave % HPW);
@@ -662,7 +662,7 @@ void fwd_split_kernel(FwdParams p) {
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // uniform per wave
     const int j = lane & 31, hh = lane >> 5;
     const int g = head / p.R;
     const int qi = q0 + j;
