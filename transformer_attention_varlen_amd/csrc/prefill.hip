@@ -502,75 +502,44 @@ void fwd_kernel(FwdParams p) {
     // before this tile's MFMA work and written to LDS after it, so the global-load latency
     // overlaps the compute.  Rows past the sequence are clamped to its last row (in bounds,
     // finite) and always masked: a tile holding them never takes the unmasked path.
-    static_assert(TBN * 16 == (TWO ? 4 : 2) * NT, "each thread stages 2 or 4 pieces per tensor");
-    const int lrow = threadIdx.x >> 4;  // rows lrow + (NT/16)i of the tile, piece threadIdx.x & 15
+    // Each thread stages PIECES 16-byte pieces of K and of V: rows lrow + (NT/16) i of the
+    // tile, dims 4 lcol .. 4 lcol+3.  Native 4-float vectors (copies of the HIP vector struct
+    // would go through private memory).
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    constexpr int PIECES = TBN * 16 / NT;
+    static_assert(PIECES * NT == TBN * 16 && PIECES >= 1, "the tile splits evenly over the threads");
+    const int lrow = threadIdx.x >> 4;
     const int lcol = threadIdx.x & 15;
     constexpr int rstep = NT / 16;
-    float4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
-    // With ROPE each K row also brings one float4 of its table row: the lanes holding dims
-    // 0..31 fetch cos, the lanes holding dims 32..63 fetch sin of the same pairs, and the two
-    // swap them (ror8) when the row is rotated at staging time.
-    float4 pt0, pt1, pt2, pt3;
+    v4 pk[PIECES], pv[PIECES];
+    // With ROPE_K each K row also brings one 4-float piece of its table row: the lanes holding
+    // dims 0..31 fetch cos, the lanes holding dims 32..63 fetch sin of the same pairs, and the
+    // two swap them (ror8) when the row is rotated at staging time.
+    v4 pt[PIECES];
     const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
-#define KATTN_TAB(R) (reinterpret_cast<const float4*>(tab + min(R, static_cast<int64_t>(p.table_len) - 1) * 32)[0])
 #define KATTN_FETCH(K0)                                                                         \
-    {                                                                                           \
-        const int64_t r0 = min((K0) + lrow, nk - 1), r1 = min((K0) + lrow + rstep, nk - 1);     \
-        pk0 = reinterpret_cast<const float4*>(kbase + r0 * p.k_stride)[lcol];                  \
-        pk1 = reinterpret_cast<const float4*>(kbase + r1 * p.k_stride)[lcol];                  \
-        pv0 = reinterpret_cast<const float4*>(vbase + r0 * p.v_stride)[lcol];                  \
-        pv1 = reinterpret_cast<const float4*>(vbase + r1 * p.v_stride)[lcol];                  \
-        if constexpr (ROPE_K) {                                                                 \
-            pt0 = KATTN_TAB(r0);                                                                \
-            pt1 = KATTN_TAB(r1);                                                                \
-        }                                                                                       \
-        if constexpr (TWO) {                                                                    \
-            const int64_t r2 = min((K0) + lrow + 2 * rstep, nk - 1);                            \
-            const int64_t r3 = min((K0) + lrow + 3 * rstep, nk - 1);                            \
-            pk2 = reinterpret_cast<const float4*>(kbase + r2 * p.k_stride)[lcol];              \
-            pk3 = reinterpret_cast<const float4*>(kbase + r3 * p.k_stride)[lcol];              \
-            pv2 = reinterpret_cast<const float4*>(vbase + r2 * p.v_stride)[lcol];              \
-            pv3 = reinterpret_cast<const float4*>(vbase + r3 * p.v_stride)[lcol];              \
-            if constexpr (ROPE_K) {                                                             \
-                pt2 = KATTN_TAB(r2);                                                            \
-                pt3 = KATTN_TAB(r3);                                                            \
-            }                                                                                   \
-        }                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
+        const int64_t r = min((K0) + lrow + rstep * i, nk - 1);                                 \
+        pk[i] = reinterpret_cast<const v4*>(kbase + r * p.k_stride)[lcol];                      \
+        pv[i] = reinterpret_cast<const v4*>(vbase + r * p.v_stride)[lcol];                      \
+        if constexpr (ROPE_K)                                                                   \
+            pt[i] = reinterpret_cast<const v4*>(                                                \
+                tab + min(r, static_cast<int64_t>(p.table_len) - 1) * 32)[0];                   \
     }
-    // rotate a staged K piece: x[i] c - x[i+32] s in the low lanes, x[i+32] c + x[i] s in the
-    // high lanes (the other half of each pair and the other table come from lane ^ 8)
-#define KATTN_ROT(X, TT)                                                                        \
-    if constexpr (ROPE_K) {                                                                       \
-        const float4 y = make_float4(ror8(X.x), ror8(X.y), ror8(X.z), ror8(X.w));               \
-        const float4 u = make_float4(ror8(TT.x), ror8(TT.y), ror8(TT.z), ror8(TT.w));           \
-        if (lcol < 8) {                                                                         \
-            X = make_float4(X.x * TT.x - y.x * u.x, X.y * TT.y - y.y * u.y,                     \
-                            X.z * TT.z - y.z * u.z, X.w * TT.w - y.w * u.w);                    \
-        } else {                                                                                \
-            X = make_float4(X.x * u.x + y.x * TT.x, X.y * u.y + y.y * TT.y,                     \
-                            X.z * u.z + y.z * TT.z, X.w * u.w + y.w * TT.w);                    \
-        }                                                                                       \
-    }
+    // rotate the staged K pieces, x[i] c - x[i+32] s in the low lanes and x[i+32] c + x[i] s in
+    // the high lanes (the other half of each pair and the other table come from lane ^ 8), then
+    // write K and V to LDS
 #define KATTN_STASH()                                                                           \
-    {                                                                                           \
-        KATTN_ROT(pk0, pt0)                                                                     \
-        KATTN_ROT(pk1, pt1)                                                                     \
-        if constexpr (TWO) {                                                                    \
-            KATTN_ROT(pk2, pt2)                                                                 \
-            KATTN_ROT(pk3, pt3)                                                                 \
+    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
+        v4 x = pk[i];                                                                           \
+        if constexpr (ROPE_K) {                                                                 \
+            const v4 tt = pt[i];                                                                \
+            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                          \
+            const v4 u = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                      \
+            x = lcol < 8 ? x * tt - y * u : x * u + y * tt;                                     \
         }                                                                                       \
-        float* kd = &Ks[lrow * LDS_STRIDE + 4 * lcol];                                          \
-        float* vd = &Vs[lrow * LDS_STRIDE + 4 * lcol];                                          \
-        *reinterpret_cast<float4*>(kd) = pk0;                                                   \
-        *reinterpret_cast<float4*>(kd + rstep * LDS_STRIDE) = pk1;                              \
-        *reinterpret_cast<float4*>(vd) = pv0;                                                   \
-        *reinterpret_cast<float4*>(vd + rstep * LDS_STRIDE) = pv1;                              \
-        if constexpr (TWO) {                                                                    \
-            *reinterpret_cast<float4*>(kd + 2 * rstep * LDS_STRIDE) = pk2;                      \
-            *reinterpret_cast<float4*>(kd + 3 * rstep * LDS_STRIDE) = pk3;                      \
-            *reinterpret_cast<float4*>(vd + 2 * rstep * LDS_STRIDE) = pv2;                      \
-            *reinterpret_cast<float4*>(vd + 3 * rstep * LDS_STRIDE) = pv3;                      \
-        }                                                                                       \
+        *reinterpret_cast<v4*>(&Ks[(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = x;            \
+        *reinterpret_cast<v4*>(&Vs[(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = pv[i];        \
     }
     // the first tile's loads go out before the Q loads, so the two latencies overlap
     KATTN_FETCH(kbeg)
@@ -607,8 +576,6 @@ void fwd_kernel(FwdParams p) {
     }
 #undef KATTN_FETCH
 #undef KATTN_STASH
-#undef KATTN_ROT
-#undef KATTN_TAB
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (qi < n) {
@@ -803,11 +770,15 @@ void fwd_split_kernel(FwdParams p) {
 struct Shape {
     int hpw, qw;
 };
-Shape pick_shape(int R) {
+// fused_banded: the fused-RoPE kernel on a sliding-window launch, which holds the table
+// registers at 3 waves/SIMD; there 2-wave work-groups (64 query rows) measured faster than
+// 4-wave ones (fewer idle tile steps per wave, more work-groups to interleave).  Causal
+// launches over long sequences keep 4-wave work-groups (measured faster).
+Shape pick_shape(int R, bool fused_banded) {
     switch (R) {
-        case 1: return {1, 4};
+        case 1: return fused_banded ? Shape{1, 2} : Shape{1, 4};
         case 2: return {2, 2};
-        case 3: return {1, 4};  // 3 heads x 32 rows would leave the 4 SIMDs unevenly loaded
+        case 3: return fused_banded ? Shape{1, 2} : Shape{1, 4};  // 3 heads x 32 rows would load the 4 SIMDs unevenly
         case 4: return {4, 1};
         default: return {1, 4};
     }
@@ -858,7 +829,9 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
 
 template <int ROT, bool F16>
 void launch_shape(const Shape& sh, const FwdParams& p, int64_t grid, hipStream_t stream) {
-    if (sh.hpw == 1) launch_fwd<1, 4, ROT, F16>(p, grid, stream);
+    if (sh.hpw == 1 && sh.qw == 2) {
+        if constexpr (ROT == 1) launch_fwd<1, 2, ROT, F16>(p, grid, stream);
+    } else if (sh.hpw == 1) launch_fwd<1, 4, ROT, F16>(p, grid, stream);
     else if (sh.hpw == 2) launch_fwd<2, 2, ROT, F16>(p, grid, stream);
     else launch_fwd<4, 1, ROT, F16>(p, grid, stream);
 }
@@ -974,17 +947,17 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
         }
     }
 
+    // Half window.  A window that reaches across the longest sequence masks nothing, so it
+    // runs as global attention (the same kernel and the same bits as window = -1).
+    const int hw = (window < 0 || window / 2 >= max_seqlen - 1) ? -1 : window / 2;
     const int R = H / G;
-    const Shape sh = pick_shape(R);
+    const Shape sh = pick_shape(R, rope && hw >= 0);
     const Geometry gm = fwd_geometry(S, T, H, sh);
     const int BM = gm.BM;
     const int64_t capacity = gm.capacity;
     const int nunits = gm.nunits;
     const int64_t grid = gm.grid;
     if (grid > 0x7fffffff) return fail(KATTN_EBOUNDS, "%s: batch too large", fn);
-    // Half window.  A window that reaches across the longest sequence masks nothing, so it
-    // runs as global attention (the same kernel and the same bits as window = -1).
-    const int hw = (window < 0 || window / 2 >= max_seqlen - 1) ? -1 : window / 2;
 
     char* ws = static_cast<char*>(workspace);
     int32_t* count = reinterpret_cast<int32_t*>(ws);
@@ -1151,7 +1124,7 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
 
     // 2. the chunk's queries against cache rows 0 .. offset + i (causal with an offset)
     const int R = H / G;
-    const Shape sh = pick_shape(R);
+    const Shape sh = pick_shape(R, false);
     const Geometry gm = fwd_geometry(B, T, H, sh);
     const int BM = gm.BM;
     const int64_t capacity = gm.capacity;
