@@ -29,6 +29,14 @@ def _gpu():
     kattn.lib()
 
 
+@pytest.fixture(params=["shared_tile_kernel", "key_split_kernel"])
+def prefill_kernel(request, monkeypatch):
+    """Runs a prefill test once with each tile kernel (the library picks by launch size;
+    KATTN_SPLIT forces the choice)."""
+    monkeypatch.setenv("KATTN_SPLIT", "0" if request.param == "shared_tile_kernel" else "1")
+    return request.param
+
+
 def oracle_prefill(case, rows=None):
     tables = oracle.rope_tables(case.theta, max(case.max_seqlen, 1))
     return oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
@@ -89,7 +97,7 @@ SMALL_CASES = [
 
 
 @pytest.mark.parametrize("lengths,H,G,window,causal", SMALL_CASES)
-def test_prefill_small_cases(lengths, H, G, window, causal):
+def test_prefill_small_cases(prefill_kernel, lengths, H, G, window, causal):
     case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
                            theta=10000.0, seed=100 + len(lengths) + H + window)
     run = gpu_prefill(case, pad_rows=5, sentinel=float("nan"))
@@ -303,7 +311,7 @@ def gpu_prefill_fused(case, pad_rows=0, sentinel=None):
 
 
 @pytest.mark.parametrize("lengths,H,G,window,causal", SMALL_CASES)
-def test_fused_rope_small_cases(lengths, H, G, window, causal):
+def test_fused_rope_small_cases(prefill_kernel, lengths, H, G, window, causal):
     case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
                            theta=10000.0, seed=200 + len(lengths) + H + window)
     run = gpu_prefill_fused(case, pad_rows=5, sentinel=float("nan"))
@@ -350,7 +358,7 @@ def _f16_bound(ref64, got16):
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("lengths,H,G,window,causal", [SMALL_CASES[2], SMALL_CASES[8],
                                                         SMALL_CASES[9], SMALL_CASES[16]])
-def test_f16_output_small_cases(fused, lengths, H, G, window, causal):
+def test_f16_output_small_cases(prefill_kernel, fused, lengths, H, G, window, causal):
     case = wl.make_prefill(lengths, H, G, packed=(H == G), window=window, causal=causal,
                            theta=10000.0, seed=300 + len(lengths) + H)
     run = PrefillRun(case)
@@ -427,7 +435,7 @@ CHUNK_CASES = [
 
 @pytest.mark.parametrize("rotate", [True, False])
 @pytest.mark.parametrize("lengths,offsets,H,G,cap", CHUNK_CASES)
-def test_prefill_cached_small_cases(rotate, lengths, offsets, H, G, cap):
+def test_prefill_cached_small_cases(prefill_kernel, rotate, lengths, offsets, H, G, cap):
     case = wl.make_chunked(lengths, offsets, H, G, cap, theta=1e5, seed=500 + H + cap)
     _check_chunk(case, rotate)
 
@@ -476,3 +484,21 @@ def test_prefill_cached_one_row_chunks_match_decode():
     assert max_err(c.out.cpu().numpy(), d.out.cpu().numpy()) <= ATOL
     assert torch.equal(c.v_cache.cpu(), d.v_cache.cpu())
     assert max_err(c.k_cache.cpu().numpy(), d.k_cache.cpu().numpy()) <= ROPE_ATOL
+
+
+@pytest.mark.parametrize("window,causal,fused", [(-1, True, False), (128, False, True),
+                                                 (-1, False, True), (40, True, False)])
+def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
+    case = wl.make_prefill([700, 33, 260], 9, 3, packed=False, window=window, causal=causal,
+                           theta=1e4, seed=90)
+    outs = []
+    for mode in ("0", "1"):
+        monkeypatch.setenv("KATTN_SPLIT", mode)
+        run = PrefillRun(case)
+        if fused:
+            run.step_fused()
+        else:
+            run.step()
+        torch.cuda.synchronize()
+        outs.append(run.out.cpu().numpy())
+    assert max_err(outs[0], outs[1]) <= ATOL

@@ -40,6 +40,15 @@ bool debug_checks() {
     return on;
 }
 
+int split_override() {
+    // read on every call so that a test can compare both kernels in one process
+    const char* e = std::getenv("KATTN_SPLIT");
+    if (e == nullptr) return -1;
+    if (std::strcmp(e, "0") == 0) return 0;
+    if (std::strcmp(e, "1") == 0) return 1;
+    return -1;
+}
+
 int check_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KATTN_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -21,6 +21,10 @@ int ok();
 // True when KATTN_CHECK=1 (read once).
 bool debug_checks();
 
+// KATTN_SPLIT=0 or 1 forces the prefill kernel choice (0: the shared-tile kernel, 1: the
+// key-split kernel); -1 (unset or any other value) leaves it to the launch size.  Testing only.
+int split_override();
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Checks the launch just queued; returns KATTN_OK or KATTN_EDEVICE.

@@ -817,7 +817,8 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     gm.BM = 32 * sh.qw;
     gm.nunits = H / sh.hpw;
     gm.capacity = tile_capacity(S, T, gm.BM);
-    gm.split = gm.capacity * gm.nunits < kSplitBelow;
+    const int forced = split_override();
+    gm.split = forced >= 0 ? forced == 1 : gm.capacity * gm.nunits < kSplitBelow;
     if (gm.split) {  // 32-row query blocks, one head per work-group
         gm.BM = 32;
         gm.nunits = H;
