@@ -189,8 +189,8 @@ def traffic_from_profiles(workload: str, kernel_source: str):
 
 
 def measure_ceilings(torch):
-    """Practical ceilings on this GPU, measured with library kernels: a cold 1 GiB read
-    (torch's sum) and a copy for HBM, a large FP32 GEMM (torch.mm) for the FP32 matrix units."""
+    """Reference rates of library kernels on this GPU: a cold 1 GiB read (torch's sum) and a
+    copy for HBM, a large FP32 GEMM (torch.mm) for the FP32 matrix units."""
     buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(buf)
     other = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -217,10 +217,11 @@ def measure_ceilings(torch):
     C = torch.empty(n, n, device="cuda")
     torch.mm(A, Bm, out=C)
     gemm_ms = best_ms(lambda: torch.mm(A, Bm, out=C), reps=3)
-    res = {"hbm_read_gbs": round(buf.numel() * 4 / (read_ms * 1e-3) / 1e9, 1),
+    res = {"torch_sum_read_gbs": round(buf.numel() * 4 / (read_ms * 1e-3) / 1e9, 1),
            "hbm_copy_gbs": round(2 * buf.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
            "fp32_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 2),
-           "how": "best of a few: torch sum over 1 GiB (cold), torch copy of 1 GiB, "
+           "how": "best of a few: torch sum over 1 GiB (cold; a library reduction, below what "
+                  "streaming reads reach), torch copy of 1 GiB (read + write bytes), "
                   "torch.mm 8192^3 FP32"}
     del buf, dst, other, A, Bm, C
     torch.cuda.empty_cache()
