@@ -3,6 +3,7 @@
 // Everything here runs on the host and touches no device memory.
 
 #include <cmath>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -38,6 +39,19 @@ bool debug_checks() {
         return e != nullptr && std::strcmp(e, "1") == 0;
     }();
     return on;
+}
+
+int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices && cache[dev].load() > 0) return cache[dev].load();
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return 256;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(cus);
+    return cus;
 }
 
 int split_override() {

@@ -21,6 +21,9 @@ int ok();
 // True when KATTN_CHECK=1 (read once).
 bool debug_checks();
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
 // KATTN_SPLIT=0 or 1 forces the prefill kernel choice (0: the shared-tile kernel, 1: the
 // key-split kernel); -1 (unset or any other value) leaves it to the launch size.  Testing only.
 int split_override();

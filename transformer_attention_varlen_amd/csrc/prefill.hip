@@ -794,10 +794,11 @@ void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
                            dim3(64 * HPW * QW), 0, stream, p);
 }
 
-// Launches with fewer work-groups than this (a quarter of the 4-wave slots of 256 CUs at 2
-// work-groups each) use the key-split kernel instead: four times the waves, each over a
-// quarter of the keys.
-constexpr int64_t kSplitBelow = 512;
+// Launches whose shared-tile work-groups would not fill one round of the GPU (4 per CU, the
+// residency of the 4-wave banded kernel) use the key-split kernel instead: four times the
+// waves, each over a quarter of the keys, so the long key ranges of a few query tiles (one
+// long sequence, or chunks continuing from long caches) are walked four ways at once.
+constexpr int kSplitWorkGroupsPerCU = 4;
 
 template <int ROT, bool F16>
 void launch_split(const FwdParams& p, int64_t grid, hipStream_t stream) {
@@ -818,7 +819,9 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     gm.nunits = H / sh.hpw;
     gm.capacity = tile_capacity(S, T, gm.BM);
     const int forced = split_override();
-    gm.split = forced >= 0 ? forced == 1 : gm.capacity * gm.nunits < kSplitBelow;
+    gm.split = forced >= 0 ? forced == 1
+                           : gm.capacity * gm.nunits <
+                                 static_cast<int64_t>(kSplitWorkGroupsPerCU) * device_cus();
     if (gm.split) {  // 32-row query blocks, one head per work-group
         gm.BM = 32;
         gm.nunits = H;
