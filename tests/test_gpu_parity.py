@@ -502,3 +502,43 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
         torch.cuda.synchronize()
         outs.append(run.out.cpu().numpy())
     assert max_err(outs[0], outs[1]) <= ATOL
+
+
+# ----------------------------------------------------------------------------- large and boundary sizes
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (1024, False)])
+def test_one_long_sequence_sampled(window, causal):
+    # one 40000-token sequence: 64-bit row offsets, long key loops, both tile kernels' range
+    n = 40000
+    case = wl.make_prefill([n], 2, 1, packed=False, window=window, causal=causal, theta=1e6,
+                           seed=95)
+    got = gpu_prefill_fused(case).out.cpu().numpy()
+    rows = np.array([0, 1, 31, 32, 33, 1023, 1024, 20000, n - 33, n - 32, n - 2, n - 1], np.int32)
+    assert max_err(got[rows], oracle_prefill(case, rows=rows)) <= ATOL
+    assert np.all(np.isfinite(got))
+
+
+def test_decode_fills_the_cache_to_capacity():
+    # used == cap: the new token lands on the last cache row
+    cap = 640
+    case = _decode_case([cap, 1, cap - 1, cap], 9, 3, cap, seed=96)
+    _check_decode(case, rotate=True)
+
+
+def test_prefill_cached_chunk_ending_on_the_last_row_of_a_large_cache():
+    cap = 16384
+    case = wl.make_chunked([700, 1], [cap - 700, cap - 1], 9, 3, cap, seed=97)
+    _check_chunk(case, rotate=True, pad_rows=0)
+
+
+def test_many_tiny_sequences_windowed():
+    # 20000 sequences of 1..3 tokens, a window, GQA: the planner's workspace prefix path
+    rng = np.random.default_rng(98)
+    lengths = rng.integers(1, 4, 20000)
+    case = wl.make_prefill(lengths, 4, 2, packed=False, window=2, causal=False, seed=99)
+    run = gpu_prefill(case, pad_rows=2, sentinel=float("nan"))
+    got = run.out_full.cpu().numpy()
+    rows = _sample_rows(case, 64, 100)[:400]
+    assert max_err(got[rows], oracle_prefill(case, rows=rows)) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))
+    assert np.all(np.isfinite(got[:case.T]))
