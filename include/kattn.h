@@ -32,9 +32,10 @@
  *   but the results are then unspecified.  With KATTN_CHECK=1 in the
  *   environment each call copies its device tables to the host, validates
  *   them and returns KATTN_EBOUNDS on a bad one (synchronous; debugging
- *   only).  KATTN_SPLIT=0 or 1 forces the prefill kernel choice (the
- *   shared-tile kernel or the key-split kernel that small launches get);
- *   results agree to rounding either way (testing only, read on every call).
+ *   only).  KATTN_SPLIT=0 forces the shared-tile prefill kernel, 1 the
+ *   key-split kernel that small launches get, 4 or 8 that kernel with 4 or 8
+ *   waves per work-group; results agree to rounding either way (testing
+ *   only, read on every call).
  *
  * Fixed shapes and graph capture
  * ------------------------------

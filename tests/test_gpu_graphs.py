@@ -6,9 +6,9 @@ fits the bucket.  Every test replays its graph several times, with new contents
 written into the device tables and inputs between replays and eager library calls
 and synchronisations in between, and checks each replay:
 
-* bit for bit against an eager call of the same bucket shape (every output row is
-  computed by one wave in a fixed key order, whatever the grid), and against the
-  rows an eager call on the exact (unpadded) shape writes;
+* bit for bit against an eager call of the same bucket shape (the same kernels and
+  the same order of summation), and within 2e-5 of an eager call on the exact
+  (unpadded) shape, which may pick another tile kernel for its smaller launch;
 * once per test against the FP64 oracle (2e-5), rows outside the real counts
   untouched.
 """
@@ -94,7 +94,7 @@ def test_fused_prefill_graph_replays_with_new_batches(H, G, window, causal, thet
         call(exact, S, T, int(lengths.max()), qq=_dev(qh), kk=_dev(kh), vv=_dev(vh),
              cc=_dev(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)))
         torch.cuda.synchronize()
-        assert torch.equal(exact.cpu(), got[:T])
+        assert float((exact.cpu() - got[:T]).abs().max()) <= ATOL
         if rep == 0:
             ref = oracle.varlen_attention(qh, kh, vh, np.concatenate([[0], np.cumsum(lengths)]),
                                           H, G, window, causal,

@@ -29,11 +29,12 @@ def _gpu():
     kattn.lib()
 
 
-@pytest.fixture(params=["shared_tile_kernel", "key_split_kernel"])
+@pytest.fixture(params=["shared_tile_kernel", "key_split_4_waves", "key_split_8_waves"])
 def prefill_kernel(request, monkeypatch):
     """Runs a prefill test once with each tile kernel (the library picks by launch size;
     KATTN_SPLIT forces the choice)."""
-    monkeypatch.setenv("KATTN_SPLIT", "0" if request.param == "shared_tile_kernel" else "1")
+    monkeypatch.setenv("KATTN_SPLIT", {"shared_tile_kernel": "0", "key_split_4_waves": "4",
+                                       "key_split_8_waves": "8"}[request.param])
     return request.param
 
 
@@ -492,7 +493,7 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
     case = wl.make_prefill([700, 33, 260], 9, 3, packed=False, window=window, causal=causal,
                            theta=1e4, seed=90)
     outs = []
-    for mode in ("0", "1"):
+    for mode in ("0", "4", "8"):
         monkeypatch.setenv("KATTN_SPLIT", mode)
         run = PrefillRun(case)
         if fused:
@@ -502,6 +503,7 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
         torch.cuda.synchronize()
         outs.append(run.out.cpu().numpy())
     assert max_err(outs[0], outs[1]) <= ATOL
+    assert max_err(outs[0], outs[2]) <= ATOL
 
 
 # ----------------------------------------------------------------------------- large and boundary sizes

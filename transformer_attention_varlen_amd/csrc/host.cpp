@@ -60,6 +60,8 @@ int split_override() {
     if (e == nullptr) return -1;
     if (std::strcmp(e, "0") == 0) return 0;
     if (std::strcmp(e, "1") == 0) return 1;
+    if (std::strcmp(e, "4") == 0) return 4;
+    if (std::strcmp(e, "8") == 0) return 8;
     return -1;
 }
 

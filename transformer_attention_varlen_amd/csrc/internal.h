@@ -24,8 +24,9 @@ bool debug_checks();
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus();
 
-// KATTN_SPLIT=0 or 1 forces the prefill kernel choice (0: the shared-tile kernel, 1: the
-// key-split kernel); -1 (unset or any other value) leaves it to the launch size.  Testing only.
+// KATTN_SPLIT forces the prefill kernel choice: 0 the shared-tile kernel, 1 the key-split
+// kernel (its width by launch size), 4 or 8 the key-split kernel with that many waves; -1
+// (unset or any other value) leaves it to the launch size.  Testing only.
 int split_override();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -607,13 +607,16 @@ void fwd_kernel(FwdParams p) {
 // LDS at the end with the log-sum-exp algebra: M = max m_w, l = sum l_w e^(m_w - M),
 // O = sum O_w e^(m_w - M) / l, wave w writing dims 16w .. 16w+15.  The per-tile math is the
 // main kernel's (tile_update).
-constexpr int kSplitWaves = 4;
 constexpr int kSplitTBN = 32;
 
-template <int ROT, bool F16>
-__global__ __launch_bounds__(64 * kSplitWaves) __attribute__((amdgpu_waves_per_eu(2)))
+// W waves per work-group (4, or 8 for launches of very few query tiles: the whole CU on one
+// query block).
+template <int ROT, bool F16, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_split_kernel(FwdParams p) {
     constexpr int TBN = kSplitTBN;
+    constexpr int kSplitWaves = W;
+    static_assert(W == 4 || W == 8, "4 or 8 waves split the keys");
     constexpr bool ROPE_K = ROT == 1;
     // per wave: K rows then V rows of its current tile; after the loop, its partial result
     __shared__ __attribute__((aligned(16))) float lds[kSplitWaves][2 * TBN * LDS_STRIDE];
@@ -727,7 +730,7 @@ void fwd_split_kernel(FwdParams p) {
 #undef KATTN_SPLIT_FETCH
 #undef KATTN_SPLIT_STASH
 
-    // merge the four partial results through LDS
+    // merge the W partial results through LDS
     __syncthreads();  // every wave is done with its staging region
     float* mine = lds[wave];
 #pragma unroll
@@ -742,28 +745,42 @@ void fwd_split_kernel(FwdParams p) {
     float M = kNegBig;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, lds[w][32 * 64 + lane]);
+    // wave w writes result rows r0 .. r0+RPW-1 of O0 and O1: dims 2*i0 .. 2*i0 + 2*RPW - 1
+    constexpr int RPW = 16 / W;
+    const int r0 = RPW * wave;
+    const int i0 = 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
     float l_tot = 0.0f;
-    float acc[8];
+    float acc[2 * RPW];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    const int r0 = 4 * wave;  // this wave writes result rows r0 .. r0+3 of O0 and O1
+    for (int k = 0; k < 2 * RPW; ++k) acc[k] = 0.0f;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
         const float* part = lds[w];
         const float f = __builtin_amdgcn_exp2f((part[32 * 64 + lane] - M) * kLog2e);
         l_tot = __builtin_fmaf(part[33 * 64 + lane] + part[33 * 64 + (lane ^ 32)], f, l_tot);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < RPW; ++k) {
             acc[2 * k] = __builtin_fmaf(part[(r0 + k) * 64 + lane], f, acc[2 * k]);
             acc[2 * k + 1] = __builtin_fmaf(part[(16 + r0 + k) * 64 + lane], f, acc[2 * k + 1]);
         }
     }
     const float inv = 1.0f / l_tot;
-    const int i0 = 8 * wave + 4 * hh;  // result rows i0..i0+3 -> dims 2*i0 .. 2*i0+7
+    const int64_t at = static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim + 2 * i0;
     const float4 a = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    const float4 b = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    store8<F16>(p.out, static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim + 2 * i0, a,
-                b);
+    if constexpr (RPW == 4) {
+        const float4 b = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+        store8<F16>(p.out, at, a, b);
+    } else if constexpr (F16) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 hv;
+        hv[0] = static_cast<_Float16>(a.x);
+        hv[1] = static_cast<_Float16>(a.y);
+        hv[2] = static_cast<_Float16>(a.z);
+        hv[3] = static_cast<_Float16>(a.w);
+        *reinterpret_cast<h4*>(static_cast<_Float16*>(p.out) + at) = hv;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + at) = a;
+    }
 }
 
 // Work-group shape per q-heads-per-kv-head ratio R: HPW heads x QW query blocks.
@@ -804,9 +821,13 @@ void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
 constexpr int kSplitWorkGroupsPerCU = 4;
 
 template <int ROT, bool F16>
-void launch_split(const FwdParams& p, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_split_kernel<ROT, F16>), dim3(static_cast<unsigned>(grid)),
-                       dim3(64 * kSplitWaves), 0, stream, p);
+void launch_split(const FwdParams& p, int64_t grid, bool wide, hipStream_t stream) {
+    if (wide)
+        hipLaunchKernelGGL((fwd_split_kernel<ROT, F16, 8>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * 8), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_split_kernel<ROT, F16, 4>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * 4), 0, stream, p);
 }
 
 // The launch geometry of a forward call: query block rows, work-groups per query block and
@@ -814,7 +835,7 @@ void launch_split(const FwdParams& p, int64_t grid, hipStream_t stream) {
 struct Geometry {
     int BM, nunits;
     int64_t capacity, grid;
-    bool split;
+    bool split, wide;  // wide: the key-split kernel with 8 waves
 };
 Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     Geometry gm;
@@ -822,7 +843,7 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     gm.nunits = H / sh.hpw;
     gm.capacity = tile_capacity(S, T, gm.BM);
     const int forced = split_override();
-    gm.split = forced >= 0 ? forced == 1
+    gm.split = forced >= 0 ? forced != 0
                            : gm.capacity * gm.nunits <
                                  static_cast<int64_t>(kSplitWorkGroupsPerCU) * device_cus();
     if (gm.split) {  // 32-row query blocks, one head per work-group
@@ -831,6 +852,9 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
         gm.capacity = tile_capacity(S, T, 32);
     }
     gm.grid = gm.capacity * gm.nunits;
+    // fewer than 2 key-split work-groups per CU: give each query block the whole CU
+    gm.wide = forced == 8 || (forced != 4 && gm.split &&
+                              gm.grid < 2 * static_cast<int64_t>(device_cus()));
     return gm;
 }
 
@@ -1003,10 +1027,10 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.causal = causal;
     p.scale = scale;
     if (gm.split) {
-        if (rope && out_f16) launch_split<1, true>(p, grid, stream);
-        else if (rope) launch_split<1, false>(p, grid, stream);
-        else if (out_f16) launch_split<0, true>(p, grid, stream);
-        else launch_split<0, false>(p, grid, stream);
+        if (rope && out_f16) launch_split<1, true>(p, grid, gm.wide, stream);
+        else if (rope) launch_split<1, false>(p, grid, gm.wide, stream);
+        else if (out_f16) launch_split<0, true>(p, grid, gm.wide, stream);
+        else launch_split<0, false>(p, grid, gm.wide, stream);
     } else if (rope && out_f16) launch_shape<1, true>(sh, p, grid, stream);
     else if (rope) launch_shape<1, false>(sh, p, grid, stream);
     else if (out_f16) launch_shape<0, true>(sh, p, grid, stream);
@@ -1174,8 +1198,8 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     p.causal = 1;
     p.scale = scale;
     if (gm.split) {
-        if (cos != nullptr) launch_split<2, false>(p, grid, stream);
-        else launch_split<0, false>(p, grid, stream);
+        if (cos != nullptr) launch_split<2, false>(p, grid, gm.wide, stream);
+        else launch_split<0, false>(p, grid, gm.wide, stream);
     } else if (cos != nullptr) launch_shape<2, false>(sh, p, grid, stream);
     else launch_shape<0, false>(sh, p, grid, stream);
     return check_launch(fn);
