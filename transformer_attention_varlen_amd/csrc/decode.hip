@@ -12,8 +12,8 @@
 //
 // * Stream-K split over keys: the rows of all (sequence, kv head) segments,
 //   end to end, are cut into equal ranges, one per wave of a persistent grid
-//   sized to the GPU's resident capacity, so every wave streams the same
-//   number of rows and none waits in a tail.  A range that crosses segments
+//   of one 4-wave work-group per CU, so every wave streams the same number
+//   of rows and none waits in a tail.  A range that crosses segments
 //   leaves one partial per piece; the combine kernel merges the pieces.
 //   Rows are read 4 per 16-byte load instruction (16 lanes per 256-byte
 //   row), so each instruction reads 1 KB of contiguous cache, through the
@@ -476,9 +476,12 @@ const void* split_kernel_for(int R) {
     }
 }
 
-// Waves of the split kernel the current device holds at once (its resident capacity), cached
-// per device and R; the persistent grid is sized to it.
-int resident_waves(int R, int* waves) {
+// Waves of the persistent split grid on the current device: one 4-wave work-group per CU
+// (cached per device and R).  With the nontemporal loads one work-group per CU (one wave per
+// SIMD) streams faster than the 3 the registers would allow (83 against 88 us on the b64
+// decode), and fewer, longer ranges leave fewer pieces to merge.  EDEVICE when the device
+// cannot hold one work-group of the kernel per CU.
+int persistent_waves(int R, int* waves) {
     constexpr int kMaxDevices = 64;
     static std::mutex mu;
     static int cache[kMaxDevices][kMaxR + 1] = {};
@@ -492,12 +495,9 @@ int resident_waves(int R, int* waves) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_for(R), 64 * kWaves, 0) !=
             hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu < 1)
         return KATTN_EDEVICE;
-    // One work-group (one wave per SIMD) per CU: with the nontemporal loads it streams
-    // faster than the 3 work-groups the registers allow (83 against 88 us on the b64 decode),
-    // and fewer, longer ranges leave fewer pieces to merge.
-    (void)per_cu;
     const int w = std::min(kMaxWaves, std::max(1, cus) * kWaves);
     if (dev >= 0 && dev < kMaxDevices) cache[dev][R] = w;
     *waves = w;
@@ -574,8 +574,8 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     }
     const int R = H / G;
     int waves = 0;
-    if (resident_waves(R, &waves) != KATTN_OK)
-        return fail(KATTN_EDEVICE, "%s: occupancy query failed", fn);
+    if (persistent_waves(R, &waves) != KATTN_OK)
+        return fail(KATTN_EDEVICE, "%s: occupancy query failed or the kernel does not fit a CU", fn);
     waves -= waves % kWaves;
 
     char* ws = static_cast<char*>(workspace);

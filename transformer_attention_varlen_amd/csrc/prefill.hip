@@ -4,7 +4,11 @@
 // plan.rs `launch_step` Attention arm, argus text.rs `block` and
 // `CausalSoftmax`): for every sequence of the packed batch and every q head,
 // softmax(scale * q k^T + M) v over that sequence's keys, with M = -inf
-// outside the window / causal limit.  q and k arrive already rotated.
+// outside the window / causal limit.  Variants: q and k rotated beforehand or
+// rotated inside the tile loads (RoPE, kime-cpu plan.rs `Ctx::step` Rope arm);
+// FP32 or binary16 output; keys from the packed batch or from preallocated
+// caches after a chunk append (argus text.rs `KvAppend` and `CausalSoftmax`
+// with an offset).
 //
 // Design for gfx950 (CDNA4, 64-wide waves, 160 KB LDS per CU):
 //
@@ -35,6 +39,9 @@
 // * A one-work-group planning kernel lists the (sequence, first query) tiles
 //   in the workspace, longest key range first, so the heavy tiles start
 //   first and the grid drains evenly.
+// * Launches whose query tiles would not fill the GPU run a key-split kernel
+//   instead: the waves of a work-group share 32 queries and split their key
+//   range, staging their own tiles, and merge the partial results in LDS.
 
 #include <algorithm>
 #include <cmath>
