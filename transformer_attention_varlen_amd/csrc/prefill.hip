@@ -249,6 +249,38 @@ __device__ inline float ror8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
+// The keys query position pq may see, as one interval [lo, lo + span] of key indices: below
+// nk, at most pq when causal, within hw of pq with a window.  A mask test is then a single
+// unsigned compare, (unsigned)(key - lo) <= span.  An empty interval (a lane past the end of
+// a chunk that the cache could not hold) starts beyond every key, so nothing passes.
+struct KeyInterval {
+    int lo;
+    unsigned span;
+};
+__device__ inline KeyInterval visible_keys(int pq, int nk, int causal, int hw) {
+    int lo = 0, hi = nk - 1;
+    if (causal) hi = min(hi, pq);
+    if (hw >= 0) {
+        lo = max(lo, pq - hw);
+        hi = min(hi, pq + hw);
+    }
+    if (hi < lo) {
+        lo = 0x40000000;
+        hi = lo;
+    }
+    return {lo, static_cast<unsigned>(hi - lo)};
+}
+
+// max and sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip)
+__device__ inline float halves_max(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float halves_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // One tile's online-softmax update for the 32 queries of a wave (column j of lane j and
 // j + 32): S^T = K Q^T on FP32 MFMA from the staged K rows, the boundary mask when the tile
 // is not fully visible (masked scores become -inf, the same as skipping them), the running
@@ -258,7 +290,7 @@ template <bool TWO>
 __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
                                             const float (&qreg)[32], f32x16& O0, f32x16& O1,
                                             float& m_run, float& l_run, bool full, int kt,
-                                            int nk, int pq, int causal, int hw, int j, int hh) {
+                                            KeyInterval vis, int j, int hh) {
     // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
     f32x16 S0, S1;
 #pragma unroll
@@ -285,22 +317,14 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
     }
 
     if (!full) {
-        // boundary tile: masked scores become -inf (the same as skipping them)
+        // boundary tile: masked scores become -inf (the same as skipping them); score r holds
+        // key kt + 8(r/4) + 4hh + (r%4), and S1 the key 32 above it
+        const int x = kt + 4 * hh - vis.lo;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key0 = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int key1 = key0 + 32;
-            bool v0 = key0 < nk, v1 = key1 < nk;
-            if (causal) {
-                v0 = v0 && key0 <= pq;
-                v1 = v1 && key1 <= pq;
-            }
-            if (hw >= 0) {
-                v0 = v0 && abs(pq - key0) <= hw;
-                v1 = v1 && abs(pq - key1) <= hw;
-            }
-            if (!v0) S0[r] = -INFINITY;
-            if (TWO && !v1) S1[r] = -INFINITY;
+            const int d0 = x + 8 * (r >> 2) + (r & 3);
+            if (static_cast<unsigned>(d0) > vis.span) S0[r] = -INFINITY;
+            if (TWO && static_cast<unsigned>(d0 + 32) > vis.span) S1[r] = -INFINITY;
         }
     }
 
@@ -312,7 +336,7 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
     const float ml = m_new * kLog2e;
@@ -480,6 +504,7 @@ void fwd_kernel(FwdParams p) {
     const bool wave_live = qa < n;
     const int qlast_w = min(qa + 31, n - 1);
     const int pa = off + qa, plast_w = off + qlast_w, pq = off + qi;  // positions
+    const KeyInterval vis = visible_keys(pq, nk, p.causal, p.hw);
 
     f32x16 O0, O1;  // O^T accumulators: rows i -> dims 2i (O0) and 2i+1 (O1), column = query j
 #pragma unroll
@@ -574,8 +599,7 @@ void fwd_kernel(FwdParams p) {
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
         if (any)
-            tile_update<TWO>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, nk, pq, p.causal, p.hw, j,
-                             hh);
+            tile_update<TWO>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, vis, j, hh);
 
         __syncthreads();  // every wave is done with this tile
         if (kt + TBN < kend) KATTN_STASH()
@@ -584,7 +608,7 @@ void fwd_kernel(FwdParams p) {
 #undef KATTN_FETCH
 #undef KATTN_STASH
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     if (qi < n) {
         const float inv = 1.0f / l_tot;
         const int64_t at = static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim;
@@ -645,6 +669,7 @@ void fwd_split_kernel(FwdParams p) {
     const int qi = q0 + j;
     const int qlast_w = min(q0 + 31, n - 1);
     const int pa = off + q0, plast_w = off + qlast_w, pq = off + qi;
+    const KeyInterval vis = visible_keys(pq, nk, p.causal, p.hw);
 
     int kbeg, kend;
     key_range(pa, off + min(q0 + 32, n), nk, p.hw, p.causal, kbeg, kend);
@@ -726,8 +751,7 @@ void fwd_split_kernel(FwdParams p) {
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
         if (any)
-            tile_update<false>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, nk, pq, p.causal,
-                               p.hw, j, hh);
+            tile_update<false>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, vis, j, hh);
         wave_sync_lds();  // this wave is done with the tile
         if (kt + TBN < t1) {
             KATTN_SPLIT_STASH()
