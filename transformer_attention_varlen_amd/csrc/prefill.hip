@@ -20,8 +20,8 @@
 //   S^T = K Q^T, with v_mfma_f32_32x32x2f32: A = 32 keys x 2 dims (LDS), B =
 //   2 dims x 32 queries (registers).  In the 32x32 result lane l holds query
 //   column l%32 and 16 key rows, so the row max over keys is 15 in-lane
-//   maxima plus one exchange with lane l^32, and the running max, sum and the
-//   rescale of O are per lane.
+//   maxima plus one v_permlane32_swap with lane l^32, and the running max,
+//   sum and the rescale of O are per lane.
 // * O^T = V^T P^T with the same instruction: the B operand P^T (2 keys x 32
 //   queries) is exactly register r of the score block -- keys 8(r/4)+(r%4)
 //   in lanes 0-31 and that +4 in lanes 32-63 -- so P never leaves registers;
@@ -35,7 +35,9 @@
 // * Key tiles outside a query block's window / causal range are never
 //   loaded (never computed, per wave); tiles inside it skip the per-element
 //   mask, and only boundary tiles set masked scores to -inf -- which gives
-//   exactly what the -inf mask gives (argus text.rs module docs).
+//   exactly what the -inf mask gives (argus text.rs module docs).  The keys a
+//   query sees form one interval, so that mask is one unsigned compare per
+//   score.
 // * A one-work-group planning kernel lists the (sequence, first query) tiles
 //   in the workspace, longest key range first, so the heavy tiles start
 //   first and the grid drains evenly.
