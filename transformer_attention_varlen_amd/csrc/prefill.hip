@@ -64,7 +64,9 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanBins = 1024;   // key-tile-count buckets (a multiple of kPlanThreads)
 
 // Workspace layout (bytes): [0,256) header (tile count), then the tile
-// prefix over sequences (S+1 ints), then the tile list (int2 each).
+// prefix over sequences (S+1 ints), then the tile list (int4 each: sequence, first query
+// row, the sequence's first packed row and its length, so a work-group needs one read of the
+// list before its data loads).
 constexpr size_t kHeader = 256;
 
 __host__ __device__ inline size_t prefix_bytes(int32_t S) {
@@ -146,12 +148,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                            const int32_t* __restrict__ kv_off,
                                                            int cap,
                                                            int32_t* __restrict__ ws_prefix,
-                                                           int2* __restrict__ tiles,
+                                                           int4* __restrict__ tiles,
                                                            int32_t* __restrict__ count,
                                                            int64_t capacity) {
     __shared__ int hist[kPlanBins];
     __shared__ int lds_pre[kPlanLdsSeqs + 1];
     __shared__ int lds_len[kPlanLdsSeqs];
+    __shared__ int lds_lo[kPlanLdsSeqs];
     __shared__ int wave_sums[kPlanThreads / 64];
     const bool in_lds = S <= kPlanLdsSeqs;
     int* pre = in_lds ? lds_pre : ws_prefix;
@@ -163,7 +166,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     int mine = 0;
     for (int s = s0; s < s1; ++s) {
         const SeqRange r = seq_range(cu, s, T);
-        if (in_lds) lds_len[s] = r.n;
+        if (in_lds) {
+            lds_len[s] = r.n;
+            lds_lo[s] = r.lo;
+        }
         mine += (r.n + BM - 1) / BM;
     }
     for (int b = tid; b < kPlanBins; b += kPlanThreads) hist[b] = 0;
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                 atomicAdd(&hist[bin], 1);
             } else {
                 const int at = atomicAdd(&hist[bin], 1);
-                tiles[at] = make_int2(s, q0);
+                tiles[at] = make_int4(s, q0, in_lds ? lds_lo[s] : seq_range(cu, s, T).lo, n);
             }
         }
         __syncthreads();
@@ -231,7 +237,7 @@ struct FwdParams {
     const float* k;
     const float* v;
     const int32_t* cu;
-    const int2* tiles;
+    const int4* tiles;  // (sequence, first query row, first packed row, length)
     const int32_t* count;
     int64_t out_stride, q_stride, k_stride, v_stride;
     const float* cos_t;  // RoPE tables [table_len][32] for the fused-rotation variants
@@ -488,10 +494,10 @@ void fwd_kernel(FwdParams p) {
 
     const int tix = blockIdx.x / p.nunits;
     const int unit = blockIdx.x - tix * p.nunits;
-    if (tix >= *p.count) return;
-    const int2 tile = p.tiles[tix];
-    const SeqRange sr = seq_range(p.cu, tile.x, p.T);
-    const int lo = sr.lo, n = sr.n, q0 = tile.y;
+    const int ntiles_all = *p.count;
+    const int4 tile = p.tiles[tix];  // in bounds for every tix of the grid; used once tix < count
+    if (tix >= ntiles_all) return;
+    const int lo = tile.z, n = tile.w, q0 = tile.y;
     int off, nk;  // query row i sits at position off + i; keys 0 .. nk-1
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
 
@@ -657,10 +663,10 @@ void fwd_split_kernel(FwdParams p) {
 
     const int tix = blockIdx.x / p.nunits;
     const int head = blockIdx.x - tix * p.nunits;
-    if (tix >= *p.count) return;
-    const int2 tile = p.tiles[tix];
-    const SeqRange sr = seq_range(p.cu, tile.x, p.T);
-    const int lo = sr.lo, n = sr.n, q0 = tile.y;
+    const int ntiles_all = *p.count;
+    const int4 tile = p.tiles[tix];  // in bounds for every tix of the grid; used once tix < count
+    if (tix >= ntiles_all) return;
+    const int lo = tile.z, n = tile.w, q0 = tile.y;
     int off, nk;
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
 
@@ -954,7 +960,7 @@ using namespace kattn;
 extern "C" size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T) {
     if (S < 0 || T < 0) return 0;
     // the smallest query block (32 rows) bounds the tile count of every shape
-    return kHeader + prefix_bytes(S) + static_cast<size_t>(tile_capacity(S, T, 32)) * sizeof(int2);
+    return kHeader + prefix_bytes(S) + static_cast<size_t>(tile_capacity(S, T, 32)) * sizeof(int4);
 }
 
 namespace {
@@ -1026,7 +1032,7 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     char* ws = static_cast<char*>(workspace);
     int32_t* count = reinterpret_cast<int32_t*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
-    int2* tiles = reinterpret_cast<int2*>(ws + kHeader + prefix_bytes(S));
+    int4* tiles = reinterpret_cast<int4*>(ws + kHeader + prefix_bytes(S));
 
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw, causal,
                        static_cast<const int32_t*>(nullptr), 0, prefix, tiles, count, capacity);
@@ -1198,7 +1204,7 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     char* ws = static_cast<char*>(workspace);
     int32_t* count = reinterpret_cast<int32_t*>(ws);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
-    int2* tiles = reinterpret_cast<int2*>(ws + kHeader + prefix_bytes(B));
+    int4* tiles = reinterpret_cast<int4*>(ws + kHeader + prefix_bytes(B));
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, B, T, BM, -1, 1,
                        offset, cap, prefix, tiles, count, capacity);
     int rc = check_launch(fn);
