@@ -44,8 +44,10 @@ PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 of each: the timed region is about 25 ms of headline steps, after as long again
+    # at full clock (a few ms of steps run before the clocks ramp measure 10 % slower)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--parts", default="2,3a,3b,4,5",
                     help="comma list of extra workloads to time, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
