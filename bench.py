@@ -370,8 +370,8 @@ def main():
                    "two_pass_ms_per_step": round(two_pass_ms, 4),
                    "graph_replay_ms_per_step": round(graph_ms, 4)},
         "roofline": {"bound": "mfma",
-                     "kernel": "fwd_kernel, fused-RoPE variant (one event pair over the timed "
-                               "steps: per step the planner, the tile kernel and the gaps)",
+                     "kernel": "band_kernel, fused-RoPE variant (one event pair over the "
+                               "timed steps: per step the sliding-window kernel and the gaps)",
                      "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": traffic_from_profiles(wl.WORKLOADS[HEADLINE].name, "prefill.hip"),

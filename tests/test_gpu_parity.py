@@ -29,12 +29,15 @@ def _gpu():
     kattn.lib()
 
 
-@pytest.fixture(params=["shared_tile_kernel", "key_split_4_waves", "key_split_8_waves"])
+@pytest.fixture(params=["shared_tile_kernel", "key_split_4_waves", "key_split_8_waves",
+                        "sliding_window_kernel"])
 def prefill_kernel(request, monkeypatch):
-    """Runs a prefill test once with each tile kernel (the library picks by launch size;
-    KATTN_SPLIT forces the choice)."""
+    """Runs a prefill test once with each tile kernel (the library picks by launch size and
+    window; KATTN_SPLIT forces the choice; the sliding-window kernel applies to packed batches
+    with a half-window of at most 64, other launches keep the library's own choice)."""
     monkeypatch.setenv("KATTN_SPLIT", {"shared_tile_kernel": "0", "key_split_4_waves": "4",
-                                       "key_split_8_waves": "8"}[request.param])
+                                       "key_split_8_waves": "8",
+                                       "sliding_window_kernel": "band"}[request.param])
     return request.param
 
 
@@ -154,18 +157,31 @@ def test_window_of_twice_the_length_is_bit_identical_to_global(causal):
 
 
 @pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (20, False)])
-def test_each_sequence_alone_is_bit_identical_to_its_rows_in_the_batch(window, causal):
+def test_each_sequence_alone_is_bit_identical_to_its_rows_in_the_batch(monkeypatch, window,
+                                                                        causal):
+    # Bitwise where the key tiles start at each sequence's first row (the shared-tile and
+    # key-split kernels).  The sliding-window kernel cuts tiles at multiples of 32 packed rows,
+    # so a sequence moved to another offset is summed in other groups: bitwise only for a
+    # sequence starting at row 0, within the tolerance otherwise.
     lengths = [70, 0, 200, 33]
     case = wl.make_prefill(lengths, 9, 3, packed=False, window=window, causal=causal, seed=6)
-    packed = gpu_prefill(case).out.cpu()
-    for s, n in enumerate(lengths):
-        lo = int(case.cu[s])
-        if n == 0:
-            continue
-        alone = wl.PrefillCase("alone", np.array([n], np.int32), np.array([0, n], np.int32),
-                               9, 3, window, causal, case.theta, case.q[lo:lo + n],
-                               case.k[lo:lo + n], case.v[lo:lo + n])
-        assert torch.equal(gpu_prefill(alone).out.cpu(), packed[lo:lo + n])
+    modes = ["0", "band"] if window >= 0 else [None]
+    for mode in modes:
+        if mode is not None:
+            monkeypatch.setenv("KATTN_SPLIT", mode)
+        packed = gpu_prefill(case).out.cpu()
+        for s, n in enumerate(lengths):
+            lo = int(case.cu[s])
+            if n == 0:
+                continue
+            alone = wl.PrefillCase("alone", np.array([n], np.int32), np.array([0, n], np.int32),
+                                   9, 3, window, causal, case.theta, case.q[lo:lo + n],
+                                   case.k[lo:lo + n], case.v[lo:lo + n])
+            got = gpu_prefill(alone).out.cpu()
+            if mode == "band" and lo % 32 != 0:
+                assert max_err(got.numpy(), packed[lo:lo + n].numpy()) <= ATOL
+            else:
+                assert torch.equal(got, packed[lo:lo + n])
 
 
 def test_gqa_matches_mha_with_repeated_kv():
@@ -493,7 +509,7 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
     case = wl.make_prefill([700, 33, 260], 9, 3, packed=False, window=window, causal=causal,
                            theta=1e4, seed=90)
     outs = []
-    for mode in ("0", "4", "8"):
+    for mode in ("0", "4", "8", "band"):
         monkeypatch.setenv("KATTN_SPLIT", mode)
         run = PrefillRun(case)
         if fused:
@@ -504,6 +520,7 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
         outs.append(run.out.cpu().numpy())
     assert max_err(outs[0], outs[1]) <= ATOL
     assert max_err(outs[0], outs[2]) <= ATOL
+    assert max_err(outs[0], outs[3]) <= ATOL
 
 
 # ----------------------------------------------------------------------------- large and boundary sizes

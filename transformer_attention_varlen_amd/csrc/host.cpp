@@ -62,6 +62,7 @@ int split_override() {
     if (std::strcmp(e, "1") == 0) return 1;
     if (std::strcmp(e, "4") == 0) return 4;
     if (std::strcmp(e, "8") == 0) return 8;
+    if (std::strcmp(e, "band") == 0) return kForceBand;
     return -1;
 }
 

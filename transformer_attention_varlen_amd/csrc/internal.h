@@ -25,8 +25,10 @@ bool debug_checks();
 int device_cus();
 
 // KATTN_SPLIT forces the prefill kernel choice: 0 the shared-tile kernel, 1 the key-split
-// kernel (its width by launch size), 4 or 8 the key-split kernel with that many waves; -1
-// (unset or any other value) leaves it to the launch size.  Testing only.
+// kernel (its width by launch size), 4 or 8 the key-split kernel with that many waves, "band"
+// (kForceBand) the sliding-window kernel where it applies; -1 (unset or any other value) leaves
+// it to the launch.  Testing only.
+constexpr int kForceBand = 2;
 int split_override();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -44,6 +44,10 @@
 // * Launches whose query tiles would not fill the GPU run a key-split kernel
 //   instead: the waves of a work-group share 32 queries and split their key
 //   range, staging their own tiles, and merge the partial results in LDS.
+// * Sliding windows of half-width up to 64 (ModernBERT's local layers) run a
+//   persistent kernel instead: a work-group walks a run of 32-row query blocks
+//   of one head with its 4 waves staggered by one tile, so every wave works at
+//   every tile step and each K/V row is staged into a 4-slot LDS ring once.
 
 #include <algorithm>
 #include <cmath>
@@ -248,6 +252,7 @@ struct FwdParams {
     int64_t kv_head_stride;  // floats between kv heads: 64 (packed rows) or cap * 64 (cache)
     int G, cap;
     int T, H, R, nunits, hw, causal;
+    int nseq;  // sequences in the batch (S); the sliding-window kernel holds cu[0..S] in LDS
     float scale;
 };
 
@@ -822,6 +827,299 @@ void fwd_split_kernel(FwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Sliding-window kernel for half-windows up to 64 keys over the packed batch.  The windows of
+// neighbouring query blocks overlap, so a kernel that gives every query block its own K/V
+// tiles reads each key row about three times and leaves waves idle on the tiles outside their
+// own band.  Here a persistent work-group of 4 waves walks a contiguous run of 32-row query
+// blocks of one head, in rounds of 4 consecutive blocks (wave w takes block b0 + 4r + w of
+// round r).  Each block needs the 32-key tiles b-2 .. b+2, so the rows and tiles are both cut
+// at multiples of 32 over the packed rows and sequence boundaries are handled per lane: a
+// query's visible keys are one interval of packed rows inside its own sequence.
+//
+// The waves are staggered by one tile: at step s of a round, wave w works on tile
+// b0 + 4r + w - 2 + s, so the 4 waves use 4 consecutive tiles and every wave works at every
+// step (none waits on a tile outside its band).  A ring of 4 LDS slots holds those tiles;
+// after each of the first 4 steps of a round the oldest tile is replaced by the next one,
+// fetched into registers during the step.  Every K/V row of the run is loaded once, and the
+// next round's Q is requested at the start of the current round.  The step after the last one
+// of a round uses the same 4 tiles, so a round of 5 steps loads 4 tiles.
+constexpr int kBandWaves = 4;
+constexpr int kBandSlots = 4;
+constexpr int kBandSteps = 5;          // tiles b-2 .. b+2 of query block b
+constexpr int kBandMaxHalf = 64;       // the widest half-window those tiles cover
+constexpr int kBandMaxSeqs = 1023;     // cu[0..S] is held in LDS
+constexpr int kBandWorkGroupsPerCU = 2;
+
+// The last s in [0, S] with cu[s] <= r: the sequence holding packed row r, or S when r lies
+// past the batch.
+__device__ inline int band_seq(const int* cuL, int S, int r) {
+    int lo = 0, hi = S;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cuL[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// One lane's query of a block: its packed row, whether it is a row of the batch, its position
+// inside its sequence, and the packed rows [ilo, ihi] of the keys it sees (ilo > ihi: none).
+struct BandQuery {
+    int row, pos, ilo, ihi;
+    bool live;
+};
+__device__ inline BandQuery band_query(const int* cuL, int S, int T, int row, int hw, int causal) {
+    BandQuery bq;
+    bq.row = row;
+    const int s = row < T ? band_seq(cuL, S, row) : S;
+    bq.live = s < S;
+    const int lo = bq.live ? cuL[s] : 0;
+    const int hi = bq.live ? cuL[s + 1] : 0;
+    bq.pos = row - lo;
+    bq.ilo = max(lo, row - hw);
+    bq.ihi = min(hi - 1, row + hw);
+    if (causal) bq.ihi = min(bq.ihi, row);
+    if (!bq.live) {
+        bq.ilo = 0x40000000;
+        bq.ihi = 0;
+    }
+    return bq;
+}
+
+// The Q slice of a lane (dims 32hh .. 32hh+31, as load_q) in two halves, so its loads can be
+// in flight during a round of tile work: band_q_issue requests the row (and, with RoPE, the
+// lane half's table row), band_q_finish rotates and scales.
+template <int ROT>
+__device__ __forceinline__ void band_q_issue(float4 (&xa)[8], float4 (&ta)[8], const FwdParams& p,
+                                             int row, int head, int pos, int hh, bool live) {
+    if (!live) return;
+    const float4* src = reinterpret_cast<const float4*>(
+        p.q + static_cast<int64_t>(row) * p.q_stride + head * kHeadDim + hh * 32);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) xa[m] = src[m];
+    if constexpr (ROT != 0) {
+        const int64_t prow = min(pos, p.table_len - 1);
+        const float4* tq =
+            reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) ta[m] = tq[m];
+    }
+}
+template <int ROT>
+__device__ __forceinline__ void band_q_finish(float (&qreg)[32], const float4 (&xa)[8],
+                                              const float4 (&ta)[8], float scale, int hh,
+                                              bool live) {
+    if (!live) {
+#pragma unroll
+        for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
+        return;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+        if constexpr (ROT != 0) {
+            // the pairs (x[i], x[i+32]): the other lane half holds the partner and the other
+            // table (low value first after the swap)
+            const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
+                                                                 __float_as_uint(xs[c]), false, false);
+                const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
+                                                                 __float_as_uint(ts[c]), false, false);
+                const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
+                const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
+                const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
+                qreg[4 * m + c] = r * scale;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qreg[4 * m + c] = xs[c] * scale;
+        }
+    }
+}
+
+template <int ROT, bool F16>
+__global__ __launch_bounds__(64 * kBandWaves) __attribute__((amdgpu_waves_per_eu(kBandWorkGroupsPerCU)))
+void band_kernel(FwdParams p) {
+    constexpr bool ROPE_K = ROT == 1;
+    constexpr int TBN = 32;
+    constexpr int NT = 64 * kBandWaves;
+    constexpr int PIECES = TBN * 16 / NT;  // 16-byte pieces of K and of V per thread and tile
+    static_assert(PIECES * NT == TBN * 16, "a tile splits evenly over the threads");
+    __shared__ __attribute__((aligned(16))) float Ks[kBandSlots][TBN * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) float Vs[kBandSlots][TBN * LDS_STRIDE];
+    __shared__ int cuL[kBandMaxSeqs + 1];
+
+    const int S = p.nseq, T = p.T, hw = p.hw, causal = p.causal;
+    for (int i = threadIdx.x; i <= S; i += NT) cuL[i] = min(max(p.cu[i], 0), T);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int j = lane & 31, hh = lane >> 5;
+    const int lrow = threadIdx.x >> 4, lcol = threadIdx.x & 15;  // staging: rows lrow + 16 i
+    constexpr int rstep = NT / 16;
+    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+    typedef float v4 __attribute__((ext_vector_type(4)));
+
+    // this work-group's run of (head, query block) units, head-major
+    const int nb = (T + TBN - 1) / TBN;
+    const int64_t units = static_cast<int64_t>(p.H) * nb;
+    const int64_t u_end = units * (blockIdx.x + 1) / gridDim.x;
+    for (int64_t u = units * blockIdx.x / gridDim.x; u < u_end;) {
+        const int head = static_cast<int>(u / nb);
+        const int b0 = static_cast<int>(u - static_cast<int64_t>(head) * nb);
+        const int b1 = static_cast<int>(min(static_cast<int64_t>(nb), b0 + (u_end - u)));
+        u += b1 - b0;
+        const int g = head / p.R;
+        const float* kbase = p.k + g * kHeadDim;
+        const float* vbase = p.v + g * kHeadDim;
+        const int tbase = b0 - 2;  // ring slot of tile t: (t - tbase) % 4
+        const int tlast = b1 + 1;  // the last tile a block of the run needs
+        const int rounds = (b1 - b0 + kBandWaves - 1) / kBandWaves;
+
+        // Rows of tile t held by this thread: 32t + lrow + rstep i, clamped into the batch
+        // (clamped rows are finite and never visible: their nominal key index lies outside
+        // every query's interval).  With RoPE on the keys, each row also brings its table piece
+        // at its position inside its own sequence.
+#define KATTN_BAND_FETCH(PK, PV, PT, AT, TILE)                                                  \
+    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
+        const int rr = min(max((TILE) * TBN + lrow + rstep * i, 0), T - 1);                     \
+        PK[(AT) + i] = reinterpret_cast<const v4*>(kbase + static_cast<int64_t>(rr) * p.k_stride)[lcol]; \
+        PV[(AT) + i] = reinterpret_cast<const v4*>(vbase + static_cast<int64_t>(rr) * p.v_stride)[lcol]; \
+        if constexpr (ROPE_K) {                                                                 \
+            while (rr >= cnext[i]) {  /* the row entered a later sequence */                    \
+                ++cseq[i];                                                                      \
+                cstart[i] = cnext[i];                                                           \
+                cnext[i] = cseq[i] < S ? cuL[cseq[i] + 1] : 0x7fffffff;                         \
+            }                                                                                   \
+            const int pr = rr - cstart[i];                                                      \
+            PT[(AT) + i] = reinterpret_cast<const v4*>(tab + static_cast<int64_t>(min(pr, p.table_len - 1)) * 32)[0]; \
+        }                                                                                       \
+    }
+    // rotate fetched K pieces in registers (x[i] c - x[i+32] s in the low lanes, x[i+32] c +
+    // x[i] s in the high lanes; the partner value and the other table come from lane ^ 8)
+#define KATTN_BAND_ROTATE(PK, PT, AT)                                                           \
+    if constexpr (ROPE_K) {                                                                     \
+        _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                    \
+            const v4 x = PK[(AT) + i], tt = PT[(AT) + i];                                       \
+            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                          \
+            const v4 uu = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                     \
+            PK[(AT) + i] = lcol < 8 ? x * tt - y * uu : x * uu + y * tt;                        \
+        }                                                                                       \
+    }
+#define KATTN_BAND_STASH(PK, PV, AT, SLOT)                                                      \
+    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
+        *reinterpret_cast<v4*>(&Ks[SLOT][(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = PK[(AT) + i]; \
+        *reinterpret_cast<v4*>(&Vs[SLOT][(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = PV[(AT) + i]; \
+    }
+
+        // With RoPE on the keys, each staged row's sequence is tracked by a cursor: the rows a
+        // thread stages only grow within a run (by 32 per tile), so the cursor moves only
+        // where a row crosses a sequence boundary (cstart = cu[cseq], cnext = cu[cseq + 1]).
+        int cseq[PIECES], cstart[PIECES], cnext[PIECES];
+        if constexpr (ROPE_K) {
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) {
+                cseq[i] = band_seq(cuL, S, min(max(tbase * TBN + lrow + rstep * i, 0), T - 1));
+                cstart[i] = cuL[cseq[i]];
+                cnext[i] = cseq[i] < S ? cuL[cseq[i] + 1] : 0x7fffffff;
+            }
+        }
+
+        // the first round's queries, then the ring's first 4 tiles (b0-2 .. b0+1)
+        BandQuery bq = band_query(cuL, S, T, (b0 + wave) * TBN + j, hw, causal);
+        float4 xa[8], ta[8];
+        band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
+        {
+            v4 ik[kBandSlots * PIECES], iv[kBandSlots * PIECES], it[kBandSlots * PIECES];
+#pragma unroll
+            for (int t = 0; t < kBandSlots; ++t) { KATTN_BAND_FETCH(ik, iv, it, t * PIECES, tbase + t) }
+#pragma unroll
+            for (int t = 0; t < kBandSlots; ++t) {
+                KATTN_BAND_ROTATE(ik, it, t * PIECES)
+                KATTN_BAND_STASH(ik, iv, t * PIECES, t)
+            }
+        }
+        float qreg[32];
+        band_q_finish<ROT>(qreg, xa, ta, p.scale, hh, bq.live);
+        __syncthreads();
+
+        v4 pk[PIECES], pv[PIECES], pt[PIECES];
+        for (int r = 0; r < rounds; ++r) {
+            const int b = b0 + kBandWaves * r + wave;  // this wave's query block
+            const bool blk_live = b < b1;
+            const KeyInterval vis = {bq.ilo, bq.ihi >= bq.ilo ? static_cast<unsigned>(bq.ihi - bq.ilo) : 0u};
+            const int ilo = bq.ilo, ihi = bq.ihi, qrow = bq.row;
+            const bool qlive = bq.live && blk_live;
+            // the next round's queries fly during this round
+            const bool more = r + 1 < rounds;
+            if (more) {
+                bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal);
+                band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
+            }
+
+            f32x16 O0, O1;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                O0[k] = 0.0f;
+                O1[k] = 0.0f;
+            }
+            float m_run = kNegBig, l_run = 0.0f;
+            for (int s = 0; s < kBandSteps; ++s) {
+                const int tn = tbase + kBandSlots + kBandWaves * r + s;  // stashed after this step
+                const bool fetch = s < kBandSteps - 1 && tn <= tlast;
+                if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
+                const int t = b - 2 + s;
+                const int k0 = t * TBN, k1 = k0 + TBN - 1;
+                const bool lane_any = ilo <= k1 && ihi >= k0;
+                const bool lane_full = ilo <= k0 && ihi >= k1;
+                const bool any = blk_live && __builtin_amdgcn_ballot_w64(lane_any) != 0;
+                const bool full = __builtin_amdgcn_ballot_w64(!lane_full) == 0;
+                if (any) {
+                    const int slot = (t - tbase) & (kBandSlots - 1);
+                    tile_update<false>(Ks[slot], Vs[slot], qreg, O0, O1, m_run, l_run, full, k0,
+                                       vis, j, hh);
+                }
+                if (fetch) {
+                    KATTN_BAND_ROTATE(pk, pt, 0)
+                    __syncthreads();  // every wave is done with the oldest tile
+                    KATTN_BAND_STASH(pk, pv, 0, (tn - tbase) & (kBandSlots - 1))
+                    __syncthreads();
+                }
+            }
+
+            const float l_tot = halves_sum(l_run);
+            if (qlive) {
+                const float inv = 1.0f / l_tot;
+                const int64_t at = static_cast<int64_t>(qrow) * p.out_stride + head * kHeadDim;
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int i0 = 8 * grp + 4 * hh;
+                    const int r0 = 4 * grp;
+                    float4 a, c;
+                    a.x = O0[r0 + 0] * inv;
+                    a.y = O1[r0 + 0] * inv;
+                    a.z = O0[r0 + 1] * inv;
+                    a.w = O1[r0 + 1] * inv;
+                    c.x = O0[r0 + 2] * inv;
+                    c.y = O1[r0 + 2] * inv;
+                    c.z = O0[r0 + 3] * inv;
+                    c.w = O1[r0 + 3] * inv;
+                    store8<F16>(p.out, at + 2 * i0, a, c);
+                }
+            }
+            if (more) band_q_finish<ROT>(qreg, xa, ta, p.scale, hh, bq.live);
+        }
+        __syncthreads();  // the next run refills every slot
+#undef KATTN_BAND_FETCH
+#undef KATTN_BAND_STASH
+#undef KATTN_BAND_ROTATE
+    }
+}
+
 // Work-group shape per q-heads-per-kv-head ratio R: HPW heads x QW query blocks.
 struct Shape {
     int hpw, qw;
@@ -881,7 +1179,7 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     gm.BM = 32 * sh.qw;
     gm.nunits = H / sh.hpw;
     gm.capacity = tile_capacity(S, T, gm.BM);
-    const int forced = split_override();
+    const int forced = split_override() == kForceBand ? -1 : split_override();
     gm.split = forced >= 0 ? forced != 0
                            : gm.capacity * gm.nunits <
                                  static_cast<int64_t>(kSplitWorkGroupsPerCU) * device_cus();
@@ -895,6 +1193,12 @@ Geometry fwd_geometry(int S, int T, int H, const Shape& sh) {
     gm.wide = forced == 8 || (forced != 4 && gm.split &&
                               gm.grid < 2 * static_cast<int64_t>(device_cus()));
     return gm;
+}
+
+template <int ROT, bool F16>
+void launch_band(const FwdParams& p, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((band_kernel<ROT, F16>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * kBandWaves), 0, stream, p);
 }
 
 template <int ROT, bool F16>
@@ -1021,6 +1325,11 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     // runs as global attention (the same kernel and the same bits as window = -1).
     const int hw = (window < 0 || window / 2 >= max_seqlen - 1) ? -1 : window / 2;
     const int R = H / G;
+    // Sliding windows of half-width up to 64 over a batch whose cu fits in LDS run on the
+    // persistent sliding-window kernel (no planning pass).
+    const int forced = split_override();
+    const bool band = hw >= 0 && hw <= kBandMaxHalf && S <= kBandMaxSeqs &&
+                      (forced == -1 || forced == kForceBand);
     const Shape sh = pick_shape(R, rope && hw >= 0);
     const Geometry gm = fwd_geometry(S, T, H, sh);
     const int BM = gm.BM;
@@ -1034,10 +1343,13 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
     int4* tiles = reinterpret_cast<int4*>(ws + kHeader + prefix_bytes(S));
 
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw, causal,
-                       static_cast<const int32_t*>(nullptr), 0, prefix, tiles, count, capacity);
-    int rc = check_launch(fn);
-    if (rc != KATTN_OK) return rc;
+    if (!band) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw,
+                           causal, static_cast<const int32_t*>(nullptr), 0, prefix, tiles, count,
+                           capacity);
+        const int rc = check_launch(fn);
+        if (rc != KATTN_OK) return rc;
+    }
 
     FwdParams p;
     p.out = out;
@@ -1065,7 +1377,19 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.hw = hw;
     p.causal = causal;
     p.scale = scale;
-    if (gm.split) {
+    p.nseq = S;
+    if (band) {
+        // a persistent grid of kBandWorkGroupsPerCU per CU, each with a run of at least one
+        // round (4 query blocks) when the batch allows
+        const int64_t units = static_cast<int64_t>(H) * ((T + 31) / 32);
+        const int64_t bgrid = std::max<int64_t>(
+            1, std::min<int64_t>(static_cast<int64_t>(kBandWorkGroupsPerCU) * device_cus(),
+                                 (units + kBandWaves - 1) / kBandWaves));
+        if (rope && out_f16) launch_band<1, true>(p, bgrid, stream);
+        else if (rope) launch_band<1, false>(p, bgrid, stream);
+        else if (out_f16) launch_band<0, true>(p, bgrid, stream);
+        else launch_band<0, false>(p, bgrid, stream);
+    } else if (gm.split) {
         if (rope && out_f16) launch_split<1, true>(p, grid, gm.wide, stream);
         else if (rope) launch_split<1, false>(p, grid, gm.wide, stream);
         else if (out_f16) launch_split<0, true>(p, grid, gm.wide, stream);
@@ -1236,6 +1560,7 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     p.hw = -1;
     p.causal = 1;
     p.scale = scale;
+    p.nseq = B;
     if (gm.split) {
         if (cos != nullptr) launch_split<2, false>(p, grid, gm.wide, stream);
         else launch_split<0, false>(p, grid, gm.wide, stream);
