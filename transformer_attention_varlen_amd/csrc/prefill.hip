@@ -253,8 +253,25 @@ struct FwdParams {
     int G, cap;
     int T, H, R, nunits, hw, causal;
     int nseq;  // sequences in the batch (S); the sliding-window kernel holds cu[0..S] in LDS
+    int bm;    // query rows per tile-list item (used when tiles is NULL)
     float scale;
 };
+
+// The work item tix: from the planner's list, or, for a batch of one sequence (tiles == NULL),
+// its query blocks in order, the heaviest first (the last block of a causal sequence sees the
+// most keys).  Returns false past the last item.
+__device__ inline bool list_tile(const FwdParams& p, int tix, int4& tile) {
+    if (p.tiles != nullptr) {
+        if (tix >= *p.count) return false;
+        tile = p.tiles[tix];
+        return true;
+    }
+    const SeqRange r = seq_range(p.cu, 0, p.T);
+    const int nblk = (r.n + p.bm - 1) / p.bm;
+    if (tix >= nblk) return false;
+    tile = make_int4(0, (p.causal ? nblk - 1 - tix : tix) * p.bm, r.lo, r.n);
+    return true;
+}
 
 // Value held by lane l ^ 8 (DPP row_ror:8 inside each 16-lane row): the lane that holds the
 // other half of a rotation pair when 16 lanes cover one 64-float row, 4 floats each.
@@ -499,9 +516,8 @@ void fwd_kernel(FwdParams p) {
 
     const int tix = blockIdx.x / p.nunits;
     const int unit = blockIdx.x - tix * p.nunits;
-    const int ntiles_all = *p.count;
-    const int4 tile = p.tiles[tix];  // in bounds for every tix of the grid; used once tix < count
-    if (tix >= ntiles_all) return;
+    int4 tile;
+    if (!list_tile(p, tix, tile)) return;
     const int lo = tile.z, n = tile.w, q0 = tile.y;
     int off, nk;  // query row i sits at position off + i; keys 0 .. nk-1
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
@@ -668,9 +684,8 @@ void fwd_split_kernel(FwdParams p) {
 
     const int tix = blockIdx.x / p.nunits;
     const int head = blockIdx.x - tix * p.nunits;
-    const int ntiles_all = *p.count;
-    const int4 tile = p.tiles[tix];  // in bounds for every tix of the grid; used once tix < count
-    if (tix >= ntiles_all) return;
+    int4 tile;
+    if (!list_tile(p, tix, tile)) return;
     const int lo = tile.z, n = tile.w, q0 = tile.y;
     int off, nk;
     key_count(p.kv_off, p.cap, tile.x, n, off, nk);
@@ -1343,7 +1358,9 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + kHeader);
     int4* tiles = reinterpret_cast<int4*>(ws + kHeader + prefix_bytes(S));
 
-    if (!band) {
+    // One sequence needs no plan: the tile kernels walk its query blocks, the heaviest first.
+    const bool planned = !band && S > 1;
+    if (planned) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, S, T, BM, hw,
                            causal, static_cast<const int32_t*>(nullptr), 0, prefix, tiles, count,
                            capacity);
@@ -1357,8 +1374,9 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.k = k;
     p.v = v;
     p.cu = cu;
-    p.tiles = tiles;
+    p.tiles = planned ? tiles : nullptr;
     p.count = count;
+    p.bm = BM;
     p.out_stride = out_stride;
     p.q_stride = q_stride;
     p.k_stride = k_stride;
@@ -1542,6 +1560,7 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     p.cu = cu;
     p.tiles = tiles;
     p.count = count;
+    p.bm = BM;
     p.out_stride = out_stride;
     p.q_stride = q_stride;
     p.k_stride = kHeadDim;
