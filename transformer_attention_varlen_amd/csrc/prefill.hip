@@ -27,9 +27,10 @@
 //   in lanes 0-31 and that +4 in lanes 32-63 -- so P never leaves registers;
 //   the A operand reads the matching V rows from LDS.
 // * The contraction order over the 64 dims is a free choice: lane half h
-//   feeds dims 32h..32h+31, so each lane's Q slice is 128 contiguous bytes
-//   and K is read as ds_read_b128.  V is read as float2 (dims 2j, 2j+1)
-//   feeding two accumulators, so output dim d = 2i + block.
+//   feeds dims 16h..16h+15 and 32+16h..32+16h+15, so each lane holds both
+//   members of its RoPE pairs (q rotates in-lane), its Q slice is two
+//   64-byte runs and K is read as ds_read_b128.  V is read as float2 (dims
+//   2j, 2j+1) feeding two accumulators, so output dim d = 2i + block.
 // * scale is folded into q as it is loaded: exact for 1/8 (argus text.rs
 //   module docs).  exp is v_exp_f32 on (s - m) * log2(e).
 // * Key tiles outside a query block's window / causal range are never
@@ -311,6 +312,12 @@ __device__ inline float halves_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// The 64 dims of a head are contracted in an order chosen so that every lane holds both
+// members of each RoPE pair (x[i], x[i+32]): lane half hh takes dims 16hh .. 16hh+15 and
+// 32+16hh .. 32+16hh+15, as eight float4 groups; group m starts dim_group(m) floats after dim
+// 16hh.  Q slices and K operand reads use the same order, so the rotation of q is in-lane.
+__host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16 : 0); }
+
 // One tile's online-softmax update for the 32 queries of a wave (column j of lane j and
 // j + 32): S^T = K Q^T on FP32 MFMA from the staged K rows, the boundary mask when the tile
 // is not fully visible (masked scores become -inf, the same as skipping them), the running
@@ -328,17 +335,19 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
         S0[r] = 0.0f;
         S1[r] = 0.0f;
     }
-    const float* k0 = &Ks[j * LDS_STRIDE + hh * 32];
-    const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 32];
+    // dims of lane half hh in contraction order: 16hh .. 16hh+15, then 32+16hh .. 32+16hh+15
+    // (both members of every RoPE pair in one lane), float4 group m at dim_group(m, hh)
+    const float* k0 = &Ks[j * LDS_STRIDE + hh * 16];
+    const float* k1 = &Ks[(32 + j) * LDS_STRIDE + hh * 16];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const float4 a0 = *reinterpret_cast<const float4*>(k0 + 4 * m);
+        const float4 a0 = *reinterpret_cast<const float4*>(k0 + dim_group(m));
         S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, qreg[4 * m + 0], S0, 0, 0, 0);
         S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, qreg[4 * m + 1], S0, 0, 0, 0);
         S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, qreg[4 * m + 2], S0, 0, 0, 0);
         S0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, qreg[4 * m + 3], S0, 0, 0, 0);
         if constexpr (TWO) {
-            const float4 a1 = *reinterpret_cast<const float4*>(k1 + 4 * m);
+            const float4 a1 = *reinterpret_cast<const float4*>(k1 + dim_group(m));
             S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, qreg[4 * m + 0], S1, 0, 0, 0);
             S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, qreg[4 * m + 1], S1, 0, 0, 0);
             S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, qreg[4 * m + 2], S1, 0, 0, 0);
@@ -413,57 +422,54 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
 // of kime-cpu plan.rs `Ctx::step` and argus text.rs `rope`, moved into the tile loads); 2,
 // only q is rotated (keys come from a cache that holds rotated rows).
 // F16: the output is written as IEEE binary16 (round to nearest even) instead of FP32.
-// The Q slice of one lane: dims 32hh .. 32hh+31 of the query in packed row `row` at
-// position pq, times scale; rotated at pq first when ROT != 0; zeros when !live.
+// The Q slice of one lane: dims 16hh .. 16hh+15 and 32+16hh .. 32+16hh+15 of the query in
+// packed row `row` (contraction order, dim_group), times scale; rotated at position pq first
+// when ROT != 0 (in-lane: the slice holds both members of each pair); zeros when !live.
 template <int ROT>
 __device__ __forceinline__ void load_q(float (&qreg)[32], const FwdParams& p, int64_t row,
                                        int head, int pq, int hh, bool live) {
     if (live) {
-        const float* qrow = p.q + row * p.q_stride + head * kHeadDim;
-        const float4* src = reinterpret_cast<const float4*>(qrow + hh * 32);
-        if constexpr (ROT != 0) {
-            // pairs (x[i], x[i+32]) at position pq: the low lane half loads dims 0..31 and the
-            // cos row, the high half dims 32..63 and the sin row; a permlane32 swap then gives
-            // every lane both members of each pair and both tables (low value first).
-            const int64_t prow = min(pq, p.table_len - 1);
-            const float4* tq = reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
-            float4 xa[8], ta[8];
+        const float* qrow = p.q + row * p.q_stride + head * kHeadDim + hh * 16;
+        float4 xa[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                xa[m] = src[m];
-                ta[m] = tq[m];
+        for (int m = 0; m < 8; ++m) xa[m] = *reinterpret_cast<const float4*>(qrow + dim_group(m));
+        if constexpr (ROT != 0) {
+            // pairs (x[i], x[i+32]) at position pq, i = 16hh .. 16hh+15: groups m and m + 4 hold
+            // the two members, cos and sin of pair i are entries i of the table rows
+            const int64_t prow = min(pq, p.table_len - 1);
+            const float4* tc = reinterpret_cast<const float4*>(p.cos_t + prow * 32 + hh * 16);
+            const float4* tsn = reinterpret_cast<const float4*>(p.sin_t + prow * 32 + hh * 16);
+            float4 ca[4], sa[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                ca[m] = tc[m];
+                sa[m] = tsn[m];
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
-                const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+            for (int m = 0; m < 4; ++m) {
+                const float lo[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+                const float hi[4] = {xa[m + 4].x, xa[m + 4].y, xa[m + 4].z, xa[m + 4].w};
+                const float cs[4] = {ca[m].x, ca[m].y, ca[m].z, ca[m].w};
+                const float sn[4] = {sa[m].x, sa[m].y, sa[m].z, sa[m].w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
-                                                                     __float_as_uint(xs[c]), false, false);
-                    const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
-                                                                     __float_as_uint(ts[c]), false, false);
-                    const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
-                    const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
-                    const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
-                    qreg[4 * m + c] = r * p.scale;
+                    qreg[4 * m + c] = (lo[c] * cs[c] - hi[c] * sn[c]) * p.scale;
+                    qreg[16 + 4 * m + c] = (hi[c] * cs[c] + lo[c] * sn[c]) * p.scale;
                 }
             }
         } else {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const float4 t = src[m];
-                qreg[4 * m + 0] = t.x * p.scale;
-                qreg[4 * m + 1] = t.y * p.scale;
-                qreg[4 * m + 2] = t.z * p.scale;
-                qreg[4 * m + 3] = t.w * p.scale;
+                qreg[4 * m + 0] = xa[m].x * p.scale;
+                qreg[4 * m + 1] = xa[m].y * p.scale;
+                qreg[4 * m + 2] = xa[m].z * p.scale;
+                qreg[4 * m + 3] = xa[m].w * p.scale;
             }
         }
     } else {
 #pragma unroll
         for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
     }
-
 }
 
 // Orders one wave's LDS accesses between its own lanes (a wave never shares its region).
@@ -605,7 +611,7 @@ void fwd_kernel(FwdParams p) {
     // the first tile's loads go out before the Q loads, so the two latencies overlap
     KATTN_FETCH(kbeg)
 
-    // Q slice: dims 32hh .. 32hh+31 of query qi, times scale.
+    // Q slice of query qi (contraction order), times scale.
     float qreg[32];
     load_q<ROT>(qreg, p, static_cast<int64_t>(lo + qi), head, pq, hh, qi < n);
 
@@ -902,55 +908,57 @@ __device__ inline BandQuery band_query(const int* cuL, int S, int T, int row, in
     return bq;
 }
 
-// The Q slice of a lane (dims 32hh .. 32hh+31, as load_q) in two halves, so its loads can be
-// in flight during a round of tile work: band_q_issue requests the row (and, with RoPE, the
-// lane half's table row), band_q_finish rotates and scales.
+// The Q slice of a lane (its dims in contraction order, as load_q) in two halves, so its loads
+// can be in flight during a round of tile work: band_q_issue requests the row (and, with RoPE,
+// the lane half's entries of the cos and sin rows), band_q_finish rotates and scales.
 template <int ROT>
 __device__ __forceinline__ void band_q_issue(float4 (&xa)[8], float4 (&ta)[8], const FwdParams& p,
                                              int row, int head, int pos, int hh, bool live) {
     if (!live) return;
-    const float4* src = reinterpret_cast<const float4*>(
-        p.q + static_cast<int64_t>(row) * p.q_stride + head * kHeadDim + hh * 32);
+    const float* src = p.q + static_cast<int64_t>(row) * p.q_stride + head * kHeadDim + hh * 16;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) xa[m] = src[m];
+    for (int m = 0; m < 8; ++m) xa[m] = *reinterpret_cast<const float4*>(src + dim_group(m));
     if constexpr (ROT != 0) {
         const int64_t prow = min(pos, p.table_len - 1);
-        const float4* tq =
-            reinterpret_cast<const float4*>((hh == 0 ? p.cos_t : p.sin_t) + prow * 32);
+        const float4* tc = reinterpret_cast<const float4*>(p.cos_t + prow * 32 + hh * 16);
+        const float4* tsn = reinterpret_cast<const float4*>(p.sin_t + prow * 32 + hh * 16);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) ta[m] = tq[m];
+        for (int m = 0; m < 4; ++m) {
+            ta[m] = tc[m];
+            ta[m + 4] = tsn[m];
+        }
     }
 }
 template <int ROT>
 __device__ __forceinline__ void band_q_finish(float (&qreg)[32], const float4 (&xa)[8],
-                                              const float4 (&ta)[8], float scale, int hh,
-                                              bool live) {
+                                              const float4 (&ta)[8], float scale, bool live) {
     if (!live) {
 #pragma unroll
         for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
         return;
     }
+    if constexpr (ROT != 0) {
+        // groups m and m + 4 hold the pair members x[i] and x[i+32]; ta[m] and ta[m+4] their
+        // cos and sin
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const float xs[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
-        if constexpr (ROT != 0) {
-            // the pairs (x[i], x[i+32]): the other lane half holds the partner and the other
-            // table (low value first after the swap)
-            const float ts[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+        for (int m = 0; m < 4; ++m) {
+            const float lo[4] = {xa[m].x, xa[m].y, xa[m].z, xa[m].w};
+            const float hi[4] = {xa[m + 4].x, xa[m + 4].y, xa[m + 4].z, xa[m + 4].w};
+            const float cs[4] = {ta[m].x, ta[m].y, ta[m].z, ta[m].w};
+            const float sn[4] = {ta[m + 4].x, ta[m + 4].y, ta[m + 4].z, ta[m + 4].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const auto xp = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[c]),
-                                                                 __float_as_uint(xs[c]), false, false);
-                const auto tp = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts[c]),
-                                                                 __float_as_uint(ts[c]), false, false);
-                const float lo_x = __uint_as_float(xp[0]), hi_x = __uint_as_float(xp[1]);
-                const float cs = __uint_as_float(tp[0]), sn = __uint_as_float(tp[1]);
-                const float r = hh == 0 ? lo_x * cs - hi_x * sn : hi_x * cs + lo_x * sn;
-                qreg[4 * m + c] = r * scale;
+                qreg[4 * m + c] = (lo[c] * cs[c] - hi[c] * sn[c]) * scale;
+                qreg[16 + 4 * m + c] = (hi[c] * cs[c] + lo[c] * sn[c]) * scale;
             }
-        } else {
+        }
+    } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) qreg[4 * m + c] = xs[c] * scale;
+        for (int m = 0; m < 8; ++m) {
+            qreg[4 * m + 0] = xa[m].x * scale;
+            qreg[4 * m + 1] = xa[m].y * scale;
+            qreg[4 * m + 2] = xa[m].z * scale;
+            qreg[4 * m + 3] = xa[m].w * scale;
         }
     }
 }
@@ -1059,7 +1067,7 @@ void band_kernel(FwdParams p) {
             }
         }
         float qreg[32];
-        band_q_finish<ROT>(qreg, xa, ta, p.scale, hh, bq.live);
+        band_q_finish<ROT>(qreg, xa, ta, p.scale, bq.live);
         __syncthreads();
 
         v4 pk[PIECES], pv[PIECES], pt[PIECES];
@@ -1126,7 +1134,7 @@ void band_kernel(FwdParams p) {
                     store8<F16>(p.out, at + 2 * i0, a, c);
                 }
             }
-            if (more) band_q_finish<ROT>(qreg, xa, ta, p.scale, hh, bq.live);
+            if (more) band_q_finish<ROT>(qreg, xa, ta, p.scale, bq.live);
         }
         __syncthreads();  // the next run refills every slot
 #undef KATTN_BAND_FETCH
