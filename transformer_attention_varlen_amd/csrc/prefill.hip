@@ -969,8 +969,10 @@ void band_kernel(FwdParams p) {
     constexpr bool ROPE_K = ROT == 1;
     constexpr int TBN = 32;
     constexpr int NT = 64 * kBandWaves;
-    constexpr int PIECES = TBN * 16 / NT;  // 16-byte pieces of K and of V per thread and tile
-    static_assert(PIECES * NT == TBN * 16, "a tile splits evenly over the threads");
+    // staging: thread tid holds row tid / 8 of a tile, 16-byte chunks c = tid % 8 and c + 8
+    // (dims 4c .. 4c+3 and 32+4c .. 32+4c+3: both members of four RoPE pairs)
+    constexpr int PIECES = 2;
+    static_assert(NT == TBN * 8, "one tile row per 8 threads");
     __shared__ __attribute__((aligned(16))) float Ks[kBandSlots][TBN * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) float Vs[kBandSlots][TBN * LDS_STRIDE];
     __shared__ int cuL[kBandMaxSeqs + 1];
@@ -982,9 +984,7 @@ void band_kernel(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int j = lane & 31, hh = lane >> 5;
-    const int lrow = threadIdx.x >> 4, lcol = threadIdx.x & 15;  // staging: rows lrow + 16 i
-    constexpr int rstep = NT / 16;
-    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+    const int srow = threadIdx.x >> 3, schunk = threadIdx.x & 7;
     typedef float v4 __attribute__((ext_vector_type(4)));
 
     // this work-group's run of (head, query block) units, head-major
@@ -1003,53 +1003,51 @@ void band_kernel(FwdParams p) {
         const int tlast = b1 + 1;  // the last tile a block of the run needs
         const int rounds = (b1 - b0 + kBandWaves - 1) / kBandWaves;
 
-        // Rows of tile t held by this thread: 32t + lrow + rstep i, clamped into the batch
-        // (clamped rows are finite and never visible: their nominal key index lies outside
-        // every query's interval).  With RoPE on the keys, each row also brings its table piece
-        // at its position inside its own sequence.
+        // Row 32t + srow of tile t, clamped into the batch (clamped rows are finite and never
+        // visible: their nominal key index lies outside every query's interval).  With RoPE on
+        // the keys, the row also brings cos and sin of its four pairs at its position inside
+        // its own sequence.
 #define KATTN_BAND_FETCH(PK, PV, PT, AT, TILE)                                                  \
-    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
-        const int rr = min(max((TILE) * TBN + lrow + rstep * i, 0), T - 1);                     \
-        PK[(AT) + i] = reinterpret_cast<const v4*>(kbase + static_cast<int64_t>(rr) * p.k_stride)[lcol]; \
-        PV[(AT) + i] = reinterpret_cast<const v4*>(vbase + static_cast<int64_t>(rr) * p.v_stride)[lcol]; \
+    {                                                                                           \
+        const int rr = min(max((TILE) * TBN + srow, 0), T - 1);                                 \
+        const v4* krow = reinterpret_cast<const v4*>(kbase + static_cast<int64_t>(rr) * p.k_stride); \
+        const v4* vrow = reinterpret_cast<const v4*>(vbase + static_cast<int64_t>(rr) * p.v_stride); \
+        PK[(AT)] = krow[schunk];                                                                \
+        PK[(AT) + 1] = krow[schunk + 8];                                                        \
+        PV[(AT)] = vrow[schunk];                                                                \
+        PV[(AT) + 1] = vrow[schunk + 8];                                                        \
         if constexpr (ROPE_K) {                                                                 \
-            while (rr >= cnext[i]) {  /* the row entered a later sequence */                    \
-                ++cseq[i];                                                                      \
-                cstart[i] = cnext[i];                                                           \
-                cnext[i] = cseq[i] < S ? cuL[cseq[i] + 1] : 0x7fffffff;                         \
+            while (rr >= cnext) {  /* the row entered a later sequence */                       \
+                ++cseq;                                                                         \
+                cstart = cnext;                                                                 \
+                cnext = cseq < S ? cuL[cseq + 1] : 0x7fffffff;                                  \
             }                                                                                   \
-            const int pr = rr - cstart[i];                                                      \
-            PT[(AT) + i] = reinterpret_cast<const v4*>(tab + static_cast<int64_t>(min(pr, p.table_len - 1)) * 32)[0]; \
+            const int64_t trow = static_cast<int64_t>(min(rr - cstart, p.table_len - 1)) * 32;  \
+            PT[(AT)] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                     \
+            PT[(AT) + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];                 \
         }                                                                                       \
     }
-    // rotate fetched K pieces in registers (x[i] c - x[i+32] s in the low lanes, x[i+32] c +
-    // x[i] s in the high lanes; the partner value and the other table come from lane ^ 8)
+    // rotate the fetched row's four pairs in registers: x[i] c - x[i+32] s, x[i+32] c + x[i] s
 #define KATTN_BAND_ROTATE(PK, PT, AT)                                                           \
     if constexpr (ROPE_K) {                                                                     \
-        _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                    \
-            const v4 x = PK[(AT) + i], tt = PT[(AT) + i];                                       \
-            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                          \
-            const v4 uu = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                     \
-            PK[(AT) + i] = lcol < 8 ? x * tt - y * uu : x * uu + y * tt;                        \
-        }                                                                                       \
+        const v4 lo = PK[(AT)], hi = PK[(AT) + 1], cs = PT[(AT)], sn = PT[(AT) + 1];            \
+        PK[(AT)] = lo * cs - hi * sn;                                                           \
+        PK[(AT) + 1] = hi * cs + lo * sn;                                                       \
     }
 #define KATTN_BAND_STASH(PK, PV, AT, SLOT)                                                      \
     _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
-        *reinterpret_cast<v4*>(&Ks[SLOT][(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = PK[(AT) + i]; \
-        *reinterpret_cast<v4*>(&Vs[SLOT][(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = PV[(AT) + i]; \
+        *reinterpret_cast<v4*>(&Ks[SLOT][srow * LDS_STRIDE + 4 * (schunk + 8 * i)]) = PK[(AT) + i]; \
+        *reinterpret_cast<v4*>(&Vs[SLOT][srow * LDS_STRIDE + 4 * (schunk + 8 * i)]) = PV[(AT) + i]; \
     }
 
-        // With RoPE on the keys, each staged row's sequence is tracked by a cursor: the rows a
+        // With RoPE on the keys, the staged row's sequence is tracked by a cursor: the rows a
         // thread stages only grow within a run (by 32 per tile), so the cursor moves only
-        // where a row crosses a sequence boundary (cstart = cu[cseq], cnext = cu[cseq + 1]).
-        int cseq[PIECES], cstart[PIECES], cnext[PIECES];
+        // where the row crosses a sequence boundary (cstart = cu[cseq], cnext = cu[cseq + 1]).
+        int cseq = 0, cstart = 0, cnext = 0x7fffffff;
         if constexpr (ROPE_K) {
-#pragma unroll
-            for (int i = 0; i < PIECES; ++i) {
-                cseq[i] = band_seq(cuL, S, min(max(tbase * TBN + lrow + rstep * i, 0), T - 1));
-                cstart[i] = cuL[cseq[i]];
-                cnext[i] = cseq[i] < S ? cuL[cseq[i] + 1] : 0x7fffffff;
-            }
+            cseq = band_seq(cuL, S, min(max(tbase * TBN + srow, 0), T - 1));
+            cstart = cuL[cseq];
+            cnext = cseq < S ? cuL[cseq + 1] : 0x7fffffff;
         }
 
         // the first round's queries, then the ring's first 4 tiles (b0-2 .. b0+1)
