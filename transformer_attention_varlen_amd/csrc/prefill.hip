@@ -274,12 +274,6 @@ __device__ inline bool list_tile(const FwdParams& p, int tix, int4& tile) {
     return true;
 }
 
-// Value held by lane l ^ 8 (DPP row_ror:8 inside each 16-lane row): the lane that holds the
-// other half of a rotation pair when 16 lanes cover one 64-float row, 4 floats each.
-__device__ inline float ror8(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-
 // The keys query position pq may see, as one interval [lo, lo + span] of key indices: below
 // nk, at most pq when causal, within hw of pq with a window.  A mask test is then a single
 // unsigned compare, (unsigned)(key - lo) <= span.  An empty interval (a lane past the end of
@@ -569,44 +563,51 @@ void fwd_kernel(FwdParams p) {
     // before this tile's MFMA work and written to LDS after it, so the global-load latency
     // overlaps the compute.  Rows past the sequence are clamped to its last row (in bounds,
     // finite) and always masked: a tile holding them never takes the unmasked path.
-    // Each thread stages PIECES 16-byte pieces of K and of V: rows lrow + (NT/16) i of the
-    // tile, dims 4 lcol .. 4 lcol+3.  Native 4-float vectors (copies of the HIP vector struct
-    // would go through private memory).
+    // Each thread stages rows srow + (NT/8) i of the tile, two 16-byte chunks of each: c and
+    // c + 8 (c = tid % 8; dims 4c .. 4c+3 and 32+4c .. 32+4c+3, both members of four RoPE
+    // pairs, so a K row rotates in-lane).  Native 4-float vectors (copies of the HIP vector
+    // struct would go through private memory).
     typedef float v4 __attribute__((ext_vector_type(4)));
-    constexpr int PIECES = TBN * 16 / NT;
-    static_assert(PIECES * NT == TBN * 16 && PIECES >= 1, "the tile splits evenly over the threads");
-    const int lrow = threadIdx.x >> 4;
-    const int lcol = threadIdx.x & 15;
-    constexpr int rstep = NT / 16;
-    v4 pk[PIECES], pv[PIECES];
-    // With ROPE_K each K row also brings one 4-float piece of its table row: the lanes holding
-    // dims 0..31 fetch cos, the lanes holding dims 32..63 fetch sin of the same pairs, and the
-    // two swap them (ror8) when the row is rotated at staging time.
-    v4 pt[PIECES];
-    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+    constexpr int ROWS = TBN * 8 / NT;
+    static_assert(ROWS * NT == TBN * 8 && ROWS >= 1, "the tile splits evenly over the threads");
+    const int srow = threadIdx.x >> 3;
+    const int schunk = threadIdx.x & 7;
+    constexpr int rstep = NT / 8;
+    v4 pk[2 * ROWS], pv[2 * ROWS];
+    // With ROPE_K each K row also brings cos and sin of its four pairs (its position is its
+    // key index).
+    v4 pt[2 * ROWS];
 #define KATTN_FETCH(K0)                                                                         \
-    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
-        const int64_t r = min((K0) + lrow + rstep * i, nk - 1);                                 \
-        pk[i] = reinterpret_cast<const v4*>(kbase + r * p.k_stride)[lcol];                      \
-        pv[i] = reinterpret_cast<const v4*>(vbase + r * p.v_stride)[lcol];                      \
-        if constexpr (ROPE_K)                                                                   \
-            pt[i] = reinterpret_cast<const v4*>(                                                \
-                tab + min(r, static_cast<int64_t>(p.table_len) - 1) * 32)[0];                   \
-    }
-    // rotate the staged K pieces, x[i] c - x[i+32] s in the low lanes and x[i+32] c + x[i] s in
-    // the high lanes (the other half of each pair and the other table come from lane ^ 8), then
-    // write K and V to LDS
-#define KATTN_STASH()                                                                           \
-    _Pragma("unroll") for (int i = 0; i < PIECES; ++i) {                                        \
-        v4 x = pk[i];                                                                           \
+    _Pragma("unroll") for (int i = 0; i < ROWS; ++i) {                                          \
+        const int64_t r = min((K0) + srow + rstep * i, nk - 1);                                 \
+        const v4* krow = reinterpret_cast<const v4*>(kbase + r * p.k_stride);                   \
+        const v4* vrow = reinterpret_cast<const v4*>(vbase + r * p.v_stride);                   \
+        pk[2 * i] = krow[schunk];                                                               \
+        pk[2 * i + 1] = krow[schunk + 8];                                                       \
+        pv[2 * i] = vrow[schunk];                                                               \
+        pv[2 * i + 1] = vrow[schunk + 8];                                                       \
         if constexpr (ROPE_K) {                                                                 \
-            const v4 tt = pt[i];                                                                \
-            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                          \
-            const v4 u = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                      \
-            x = lcol < 8 ? x * tt - y * u : x * u + y * tt;                                     \
+            const int64_t trow = min(r, static_cast<int64_t>(p.table_len) - 1) * 32;           \
+            pt[2 * i] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                    \
+            pt[2 * i + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];                \
         }                                                                                       \
-        *reinterpret_cast<v4*>(&Ks[(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = x;            \
-        *reinterpret_cast<v4*>(&Vs[(lrow + rstep * i) * LDS_STRIDE + 4 * lcol]) = pv[i];        \
+    }
+    // rotate the staged K rows' pairs, x[i] c - x[i+32] s and x[i+32] c + x[i] s, then write K
+    // and V to LDS
+#define KATTN_STASH()                                                                           \
+    _Pragma("unroll") for (int i = 0; i < ROWS; ++i) {                                          \
+        v4 lo = pk[2 * i], hi = pk[2 * i + 1];                                                  \
+        if constexpr (ROPE_K) {                                                                 \
+            const v4 cs = pt[2 * i], sn = pt[2 * i + 1], x = lo;                                \
+            lo = x * cs - hi * sn;                                                              \
+            hi = hi * cs + x * sn;                                                              \
+        }                                                                                       \
+        float* krow = &Ks[(srow + rstep * i) * LDS_STRIDE + 4 * schunk];                        \
+        float* vrow = &Vs[(srow + rstep * i) * LDS_STRIDE + 4 * schunk];                        \
+        *reinterpret_cast<v4*>(krow) = lo;                                                      \
+        *reinterpret_cast<v4*>(krow + 32) = hi;                                                 \
+        *reinterpret_cast<v4*>(vrow) = pv[2 * i];                                               \
+        *reinterpret_cast<v4*>(vrow + 32) = pv[2 * i + 1];                                      \
     }
     // the first tile's loads go out before the Q loads, so the two latencies overlap
     KATTN_FETCH(kbeg)
@@ -725,33 +726,42 @@ void fwd_split_kernel(FwdParams p) {
     float* Ks = lds[wave];
     float* Vs = lds[wave] + TBN * LDS_STRIDE;
 
-    // staging: 16 lanes per row, rows lrow + 4i of the tile.  Native 4-float vectors: copies of
-    // the HIP vector struct would go through private memory.
+    // staging: 8 lanes per row, rows srow + 8i of the tile, chunks c and c + 8 of each (both
+    // members of four RoPE pairs, so a K row rotates in-lane).  Native 4-float vectors: copies
+    // of the HIP vector struct would go through private memory.
     typedef float v4 __attribute__((ext_vector_type(4)));
-    const int lrow = lane >> 4, lcol = lane & 15;
-    constexpr int kPieces = TBN / 4;
-    v4 pk[kPieces], pv[kPieces], pt[kPieces];
-    const float* tab = (lcol < 8 ? p.cos_t : p.sin_t) + 4 * (lcol & 7);
+    const int srow = lane >> 3, schunk = lane & 7;
+    constexpr int kRows = TBN / 8;
+    v4 pk[2 * kRows], pv[2 * kRows], pt[2 * kRows];
 #define KATTN_SPLIT_FETCH(K0)                                                                    \
-    _Pragma("unroll") for (int i = 0; i < kPieces; ++i) {                                        \
-        const int64_t r = min((K0) + lrow + 4 * i, nk - 1);                                      \
-        pk[i] = reinterpret_cast<const v4*>(kbase + r * p.k_stride)[lcol];                       \
-        pv[i] = reinterpret_cast<const v4*>(vbase + r * p.v_stride)[lcol];                       \
-        if constexpr (ROPE_K)                                                                    \
-            pt[i] = reinterpret_cast<const v4*>(                                                 \
-                tab + min(r, static_cast<int64_t>(p.table_len) - 1) * 32)[0];                    \
+    _Pragma("unroll") for (int i = 0; i < kRows; ++i) {                                          \
+        const int64_t r = min((K0) + srow + 8 * i, nk - 1);                                      \
+        const v4* krow = reinterpret_cast<const v4*>(kbase + r * p.k_stride);                    \
+        const v4* vrow = reinterpret_cast<const v4*>(vbase + r * p.v_stride);                    \
+        pk[2 * i] = krow[schunk];                                                                \
+        pk[2 * i + 1] = krow[schunk + 8];                                                        \
+        pv[2 * i] = vrow[schunk];                                                                \
+        pv[2 * i + 1] = vrow[schunk + 8];                                                        \
+        if constexpr (ROPE_K) {                                                                  \
+            const int64_t trow = min(r, static_cast<int64_t>(p.table_len) - 1) * 32;            \
+            pt[2 * i] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                     \
+            pt[2 * i + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];                 \
+        }                                                                                        \
     }
 #define KATTN_SPLIT_STASH()                                                                      \
-    _Pragma("unroll") for (int i = 0; i < kPieces; ++i) {                                        \
-        v4 x = pk[i];                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kRows; ++i) {                                          \
+        v4 lo = pk[2 * i], hi = pk[2 * i + 1];                                                   \
         if constexpr (ROPE_K) {                                                                  \
-            const v4 tt = pt[i];                                                                 \
-            const v4 y = {ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};                           \
-            const v4 u = {ror8(tt.x), ror8(tt.y), ror8(tt.z), ror8(tt.w)};                       \
-            x = lcol < 8 ? x * tt - y * u : x * u + y * tt;                                      \
+            const v4 cs = pt[2 * i], sn = pt[2 * i + 1], x = lo;                                 \
+            lo = x * cs - hi * sn;                                                               \
+            hi = hi * cs + x * sn;                                                               \
         }                                                                                        \
-        *reinterpret_cast<v4*>(&Ks[(lrow + 4 * i) * LDS_STRIDE + 4 * lcol]) = x;                 \
-        *reinterpret_cast<v4*>(&Vs[(lrow + 4 * i) * LDS_STRIDE + 4 * lcol]) = pv[i];             \
+        float* krow = &Ks[(srow + 8 * i) * LDS_STRIDE + 4 * schunk];                             \
+        float* vrow = &Vs[(srow + 8 * i) * LDS_STRIDE + 4 * schunk];                             \
+        *reinterpret_cast<v4*>(krow) = lo;                                                       \
+        *reinterpret_cast<v4*>(krow + 32) = hi;                                                  \
+        *reinterpret_cast<v4*>(vrow) = pv[2 * i];                                                \
+        *reinterpret_cast<v4*>(vrow + 32) = pv[2 * i + 1];                                       \
     }
 
     if (t0 < t1) {
