@@ -34,7 +34,9 @@
  *   them and returns KATTN_EBOUNDS on a bad one (synchronous; debugging
  *   only).  KATTN_SPLIT=0 forces the shared-tile prefill kernel, 1 the
  *   key-split kernel that small launches get, 4 or 8 that kernel with 4 or 8
- *   waves per work-group; results agree to rounding either way (testing
+ *   waves per work-group, "band" the persistent sliding-window kernel that
+ *   packed batches with a half-window of at most 64 and at most 1023
+ *   sequences get by default; results agree to rounding either way (testing
  *   only, read on every call).
  *
  * Fixed shapes and graph capture
@@ -154,7 +156,9 @@ size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T);
  *   causal:     0 or 1.
  *   scale:      finite, > 0; folded into q as it is loaded (exact for 1/8).
  *   workspace:  device, >= kattn_varlen_fwd_workspace(S, T) bytes, 256-byte
- *               aligned; holds the query-tile schedule built on the device.
+ *               aligned; holds the query-tile schedule built on the device
+ *               (sliding-window launches and one-sequence batches schedule
+ *               without it, but it is required all the same).
  * T == 0 or S == 0 queues nothing.
  * Errors: EINVAL, EUNSUPPORTED (head_dim, H % G, alignment), EBOUNDS
  * (stride narrower than the row, max_seqlen > T, workspace), EDEVICE.
