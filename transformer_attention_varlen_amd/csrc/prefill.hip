@@ -897,13 +897,21 @@ __device__ inline int band_seq(const int* cuL, int S, int r) {
 // One lane's query of a block: its packed row, whether it is a row of the batch, its position
 // inside its sequence, and the packed rows [ilo, ihi] of the keys it sees (ilo > ihi: none).
 struct BandQuery {
-    int row, pos, ilo, ihi;
+    int row, pos, ilo, ihi, seq;
     bool live;
 };
-__device__ inline BandQuery band_query(const int* cuL, int S, int T, int row, int hw, int causal) {
+// from: a sequence index with cu[from] <= row (the previous block's sequence, since a lane's
+// rows only grow within a run); the lookup walks forward from it, usually by none or one.
+__device__ inline BandQuery band_query(const int* cuL, int S, int T, int row, int hw, int causal,
+                                       int from) {
     BandQuery bq;
     bq.row = row;
-    const int s = row < T ? band_seq(cuL, S, row) : S;
+    int s = from;
+    if (row < T) {
+        while (s < S && cuL[s + 1] <= row) ++s;
+    }
+    bq.seq = s;
+    if (row >= T) s = S;
     bq.live = s < S;
     const int lo = bq.live ? cuL[s] : 0;
     const int hi = bq.live ? cuL[s + 1] : 0;
@@ -1061,7 +1069,8 @@ void band_kernel(FwdParams p) {
         }
 
         // the first round's queries, then the ring's first 4 tiles (b0-2 .. b0+1)
-        BandQuery bq = band_query(cuL, S, T, (b0 + wave) * TBN + j, hw, causal);
+        const int row0 = (b0 + wave) * TBN + j;
+        BandQuery bq = band_query(cuL, S, T, row0, hw, causal, band_seq(cuL, S, min(row0, T - 1)));
         float4 xa[8], ta[8];
         band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
         {
@@ -1088,7 +1097,7 @@ void band_kernel(FwdParams p) {
             // the next round's queries fly during this round
             const bool more = r + 1 < rounds;
             if (more) {
-                bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal);
+                bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal, bq.seq);
                 band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
             }
 
