@@ -881,6 +881,7 @@ constexpr int kBandSteps = 5;          // tiles b-2 .. b+2 of query block b
 constexpr int kBandMaxHalf = 64;       // the widest half-window those tiles cover
 constexpr int kBandMaxSeqs = 1023;     // cu[0..S] is held in LDS
 constexpr int kBandWorkGroupsPerCU = 2;
+constexpr int kBandQStep = 2;  // the step of a round that requests the next round's Q
 
 // The last s in [0, S] with cu[s] <= r: the sequence holding packed row r, or S when r lies
 // past the batch.
@@ -1094,12 +1095,7 @@ void band_kernel(FwdParams p) {
             const KeyInterval vis = {bq.ilo, bq.ihi >= bq.ilo ? static_cast<unsigned>(bq.ihi - bq.ilo) : 0u};
             const int ilo = bq.ilo, ihi = bq.ihi, qrow = bq.row;
             const bool qlive = bq.live && blk_live;
-            // the next round's queries fly during this round
             const bool more = r + 1 < rounds;
-            if (more) {
-                bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal, bq.seq);
-                band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
-            }
 
             f32x16 O0, O1;
 #pragma unroll
@@ -1112,6 +1108,13 @@ void band_kernel(FwdParams p) {
                 const int tn = tbase + kBandSlots + kBandWaves * r + s;  // stashed after this step
                 const bool fetch = s < kBandSteps - 1 && tn <= tlast;
                 if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
+                // the next round's queries are requested mid-round: early enough to land, late
+                // enough not to hold their registers through the whole round (measured against
+                // steps 0, 3 and 4)
+                if (more && s == kBandQStep) {
+                    bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal, bq.seq);
+                    band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
+                }
                 const int t = b - 2 + s;
                 const int k0 = t * TBN, k1 = k0 + TBN - 1;
                 const bool lane_any = ilo <= k1 && ihi >= k0;
