@@ -873,7 +873,7 @@ void fwd_split_kernel(FwdParams p) {
 // step (none waits on a tile outside its band).  A ring of 4 LDS slots holds those tiles;
 // after each of the first 4 steps of a round the oldest tile is replaced by the next one,
 // fetched into registers during the step.  Every K/V row of the run is loaded once, and the
-// next round's Q is requested at the start of the current round.  The step after the last one
+// next round's Q is requested during the current round.  The step after the last one
 // of a round uses the same 4 tiles, so a round of 5 steps loads 4 tiles.
 constexpr int kBandWaves = 4;
 constexpr int kBandSlots = 4;
