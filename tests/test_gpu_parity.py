@@ -561,3 +561,27 @@ def test_many_tiny_sequences_windowed():
     assert max_err(got[rows], oracle_prefill(case, rows=rows)) <= ATOL
     assert np.all(np.isnan(got[case.T:]))
     assert np.all(np.isfinite(got[:case.T]))
+
+
+@pytest.mark.parametrize("S", [1023, 1024])
+@pytest.mark.parametrize("fused", [False, True])
+def test_sliding_window_kernel_at_its_sequence_limit(S, fused):
+    # Up to 1023 sequences the sliding-window kernel holds cu in LDS; 1024 fall back to the
+    # shared-tile kernel.  Lengths 0..9 (empty sequences included) put several sequence
+    # boundaries inside every 32-row tile, so the staged rows' and the queries' sequence
+    # cursors cross many boundaries per step; half-window 4.
+    rng = np.random.default_rng(400 + S)
+    lengths = rng.integers(0, 10, S)
+    lengths[rng.integers(0, S, 40)] = 0
+    case = wl.make_prefill(lengths, 4, 2, packed=False, window=8, causal=bool(S % 2),
+                           theta=1e4, seed=401 + S)
+    run = PrefillRun(case, out_pad_rows=2)
+    run.out_full.fill_(float("nan"))
+    if fused:
+        run.step_fused()
+    else:
+        run.step()
+    torch.cuda.synchronize()
+    got = run.out_full.cpu().numpy()
+    assert max_err(got[:case.T], oracle_prefill(case)) <= ATOL
+    assert np.all(np.isnan(got[case.T:]))
