@@ -317,13 +317,15 @@ __host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16
 // is not fully visible (masked scores become -inf, the same as skipping them), the running
 // max and sum, and O^T += V^T P^T from the staged V rows.  TWO: a 64-key tile (two 32-key
 // score blocks).
+// tile_scores is the part up to the P.V product (scores, mask, running max and sum, rescale of
+// O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue loads between
+// the two.
 template <bool TWO>
-__device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
-                                            const float (&qreg)[32], f32x16& O0, f32x16& O1,
-                                            float& m_run, float& l_run, bool full, int kt,
-                                            KeyInterval vis, int j, int hh) {
+__device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
+                                            f32x16& S1, f32x16& O0, f32x16& O1, float& m_run,
+                                            float& l_run, bool full, int kt, KeyInterval vis,
+                                            int j, int hh) {
     // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
-    f32x16 S0, S1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         S0[r] = 0.0f;
@@ -390,7 +392,11 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
         O0[r] *= alpha;
         O1[r] *= alpha;
     }
+}
 
+template <bool TWO>
+__device__ __forceinline__ void tile_pv(const float* Vs, const f32x16& S0, const f32x16& S1,
+                                        f32x16& O0, f32x16& O1, int j, int hh) {
     // O^T += V^T P^T: step r takes keys 8(r/4)+(r%4) (lanes 0-31) and +4 (lanes 32-63)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -405,6 +411,16 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
             O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vb.y, S1[r], O1, 0, 0, 0);
         }
     }
+}
+
+template <bool TWO>
+__device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
+                                            const float (&qreg)[32], f32x16& O0, f32x16& O1,
+                                            float& m_run, float& l_run, bool full, int kt,
+                                            KeyInterval vis, int j, int hh) {
+    f32x16 S0, S1;
+    tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+    tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 }
 
 // TBN: keys per K/V tile.  Global launches use 64-key tiles (two 32-key score blocks per MFMA
@@ -619,8 +635,6 @@ void fwd_kernel(FwdParams p) {
     KATTN_STASH()
     __syncthreads();
     for (int kt = kbeg; kt < kend; kt += TBN) {
-        // the next tile's rows (the last trip re-reads this tile's, which are in cache)
-        KATTN_FETCH(min(kt + TBN, kend - 1))
 
         // Does this wave see some key of the tile, and does it see every one of them?
         const int klast = kt + TBN - 1;
@@ -634,8 +648,13 @@ void fwd_kernel(FwdParams p) {
             any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
-        if (any)
-            tile_update<TWO>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        // The next tile's rows (the last trip re-reads this tile's, which are in cache) are
+        // requested between the scores and the P.V product: the P.V half covers their latency,
+        // and their registers are not held through the score MFMAs.
+        f32x16 S0, S1;
+        if (any) tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        KATTN_FETCH(min(kt + TBN, kend - 1))
+        if (any) tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 
         __syncthreads();  // every wave is done with this tile
         if (kt + TBN < kend) KATTN_STASH()
