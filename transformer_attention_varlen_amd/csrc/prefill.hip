@@ -801,9 +801,6 @@ void fwd_split_kernel(FwdParams p) {
         wave_sync_lds();
     }
     for (int kt = t0; kt < t1; kt += TBN) {
-        if (kt + TBN < t1) {  // the next tile's rows fly during this tile's math
-            KATTN_SPLIT_FETCH(kt + TBN)
-        }
         const int klast = kt + TBN - 1;
         bool any = kt < nk, full = klast < nk;
         if (p.causal) {
@@ -814,8 +811,13 @@ void fwd_split_kernel(FwdParams p) {
             any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
-        if (any)
-            tile_update<false>(Ks, Vs, qreg, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        // the next tile's rows are requested between the scores and the P.V product
+        f32x16 S0, S1;
+        if (any) tile_scores<false>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        if (kt + TBN < t1) {
+            KATTN_SPLIT_FETCH(kt + TBN)
+        }
+        if (any) tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         wave_sync_lds();  // this wave is done with the tile
         if (kt + TBN < t1) {
             KATTN_SPLIT_STASH()
@@ -1127,7 +1129,6 @@ void band_kernel(FwdParams p) {
             for (int s = 0; s < kBandSteps; ++s) {
                 const int tn = tbase + kBandSlots + kBandWaves * r + s;  // stashed after this step
                 const bool fetch = s < kBandSteps - 1 && tn <= tlast;
-                if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
                 // the next round's queries are requested mid-round: early enough to land, late
                 // enough not to hold their registers through the whole round (measured against
                 // steps 0, 3 and 4)
@@ -1141,11 +1142,14 @@ void band_kernel(FwdParams p) {
                 const bool lane_full = ilo <= k0 && ihi >= k1;
                 const bool any = blk_live && __builtin_amdgcn_ballot_w64(lane_any) != 0;
                 const bool full = __builtin_amdgcn_ballot_w64(!lane_full) == 0;
-                if (any) {
-                    const int slot = (t - tbase) & (kBandSlots - 1);
-                    tile_update<false>(Ks[slot], Vs[slot], qreg, O0, O1, m_run, l_run, full, k0,
+                // the next tile's rows are requested between the scores and the P.V product
+                const int slot = (t - tbase) & (kBandSlots - 1);
+                f32x16 S0, S1;
+                if (any)
+                    tile_scores<false>(Ks[slot], qreg, S0, S1, O0, O1, m_run, l_run, full, k0,
                                        vis, j, hh);
-                }
+                if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
+                if (any) tile_pv<false>(Vs[slot], S0, S1, O0, O1, j, hh);
                 if (fetch) {
                     KATTN_BAND_ROTATE(pk, pt, 0)
                     __syncthreads();  // every wave is done with the oldest tile
