@@ -387,10 +387,15 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
         }
     }
     l_run = l_run * alpha + psum;
+    // With 64-key tiles (long global and causal rows) the running max rarely moves after the
+    // first tiles: the rescale is skipped when it moved in no lane (alpha is then exactly 1, so
+    // the result is unchanged).  On 32-key tiles the test measured slower than the multiplies.
+    if (!TWO || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        O0[r] *= alpha;
-        O1[r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+            O0[r] *= alpha;
+            O1[r] *= alpha;
+        }
     }
 }
 
