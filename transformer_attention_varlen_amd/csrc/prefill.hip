@@ -1033,15 +1033,16 @@ void band_kernel(FwdParams p) {
     const int srow = threadIdx.x >> 3, schunk = threadIdx.x & 7;
     typedef float v4 __attribute__((ext_vector_type(4)));
 
-    // this work-group's run of (head, query block) units, head-major
+    // This work-group's run: query blocks [b0, b1) of one head.  Each head's blocks are cut
+    // into p.nunits equal runs, so no run crosses a head (a crossing run would pay a second
+    // ring fill, and the launch ends with its slowest work-group).
     const int nb = (T + TBN - 1) / TBN;
-    const int64_t units = static_cast<int64_t>(p.H) * nb;
-    const int64_t u_end = units * (blockIdx.x + 1) / gridDim.x;
-    for (int64_t u = units * blockIdx.x / gridDim.x; u < u_end;) {
-        const int head = static_cast<int>(u / nb);
-        const int b0 = static_cast<int>(u - static_cast<int64_t>(head) * nb);
-        const int b1 = static_cast<int>(min(static_cast<int64_t>(nb), b0 + (u_end - u)));
-        u += b1 - b0;
+    const int head = blockIdx.x / p.nunits;
+    const int run = blockIdx.x - head * p.nunits;
+    {
+        const int b0 = static_cast<int>(static_cast<int64_t>(nb) * run / p.nunits);
+        const int b1 = static_cast<int>(static_cast<int64_t>(nb) * (run + 1) / p.nunits);
+        if (b0 >= b1) return;
         const int g = head / p.R;
         const float* kbase = p.k + g * kHeadDim;
         const float* vbase = p.v + g * kHeadDim;
@@ -1454,12 +1455,15 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.scale = scale;
     p.nseq = S;
     if (band) {
-        // a persistent grid of kBandWorkGroupsPerCU per CU, each with a run of at least one
-        // round (4 query blocks) when the batch allows
-        const int64_t units = static_cast<int64_t>(H) * ((T + 31) / 32);
-        const int64_t bgrid = std::max<int64_t>(
-            1, std::min<int64_t>(static_cast<int64_t>(kBandWorkGroupsPerCU) * device_cus(),
-                                 (units + kBandWaves - 1) / kBandWaves));
+        // a persistent grid of up to kBandWorkGroupsPerCU per CU: each head's query blocks cut
+        // into the same number of runs, each of at least one round (4 blocks) when the batch
+        // allows
+        const int64_t nb = (T + 31) / 32;
+        const int64_t slots = static_cast<int64_t>(kBandWorkGroupsPerCU) * device_cus();
+        const int64_t runs = std::max<int64_t>(
+            1, std::min<int64_t>(slots / H, (nb + kBandWaves - 1) / kBandWaves));
+        p.nunits = static_cast<int>(runs);
+        const int64_t bgrid = runs * H;
         if (rope && out_f16) launch_band<1, true>(p, bgrid, stream);
         else if (rope) launch_band<1, false>(p, bgrid, stream);
         else if (out_f16) launch_band<0, true>(p, bgrid, stream);
