@@ -525,9 +525,11 @@ def test_both_tile_kernels_agree(monkeypatch, window, causal, fused):
 
 # ----------------------------------------------------------------------------- large and boundary sizes
 
-@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (1024, False)])
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (1024, False), (128, False),
+                                           (128, True)])
 def test_one_long_sequence_sampled(window, causal):
-    # one 40000-token sequence: 64-bit row offsets, long key loops, both tile kernels' range
+    # one 40000-token sequence: 64-bit row offsets, long key loops, both tile kernels' range;
+    # window 128 runs the sliding-window kernel over runs of about 60 blocks
     n = 40000
     case = wl.make_prefill([n], 2, 1, packed=False, window=window, causal=causal, theta=1e6,
                            seed=95)
