@@ -914,7 +914,7 @@ constexpr int kBandSteps = 5;          // tiles b-2 .. b+2 of query block b
 constexpr int kBandMaxHalf = 64;       // the widest half-window those tiles cover
 constexpr int kBandMaxSeqs = 1023;     // cu[0..S] is held in LDS
 constexpr int kBandWorkGroupsPerCU = 2;
-constexpr int kBandQStep = 2;  // the step of a round that requests the next round's Q
+constexpr int kBandQStep = 1;  // the step of a round that requests the next round's Q
 
 // The last s in [0, S] with cu[s] <= r: the sequence holding packed row r, or S when r lies
 // past the batch.
@@ -1138,12 +1138,14 @@ void band_kernel(FwdParams p) {
                 O1[k] = 0.0f;
             }
             float m_run = kNegBig, l_run = 0.0f;
+            // unrolled: the compiler schedules across the five steps (1 % on the two-pass form)
+#pragma unroll
             for (int s = 0; s < kBandSteps; ++s) {
                 const int tn = tbase + kBandSlots + kBandWaves * r + s;  // stashed after this step
                 const bool fetch = s < kBandSteps - 1 && tn <= tlast;
-                // the next round's queries are requested mid-round: early enough to land, late
+                // the next round's queries are requested at step 1: early enough to land, late
                 // enough not to hold their registers through the whole round (measured against
-                // steps 0, 3 and 4)
+                // steps 0, 2, 3 and 4)
                 if (more && s == kBandQStep) {
                     bq = band_query(cuL, S, T, (b + kBandWaves) * TBN + j, hw, causal, bq.seq);
                     band_q_issue<ROT>(xa, ta, p, bq.row, head, bq.pos, hh, bq.live);
