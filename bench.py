@@ -38,7 +38,8 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 HEADLINE = "1"
 PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
-         "3b": "prefill_causal_16x2048", "4": "decode_b64", "5": "chunked_prefill_b16"}
+         "3b": "prefill_causal_16x2048", "3c": "prefill_causal_1142_plus_16x2048",
+         "4": "decode_b64", "5": "chunked_prefill_b16"}
 
 
 def parse():
@@ -48,12 +49,12 @@ def parse():
     # at full clock (a few ms of steps run before the clocks ramp measure 10 % slower)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--parts", default="2,3a,3b,4,5",
+    ap.add_argument("--parts", default="2,3a,3b,3c,4,5",
                     help="comma list of extra workloads to time, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 disables)")
     ap.add_argument("--only", default=None,
-                    help="run only this workload's loop (for profiling): 1, 2, 3a, 3b, 4 or 5")
+                    help="run only this workload's loop (for profiling): 1, 2, 3a, 3b, 3c, 4 or 5")
     ap.add_argument("--fused", action="store_true",
                     help="with --only: loop the fused-RoPE step instead of prologue + attention")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

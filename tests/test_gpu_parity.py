@@ -133,7 +133,7 @@ def _sample_rows(case, n_random, seed):
     return np.array(sorted(r for r in rows if 0 <= r < case.T), np.int32)
 
 
-@pytest.mark.parametrize("key", ["2", "3b"])
+@pytest.mark.parametrize("key", ["2", "3b", "3c"])
 def test_workload_sampled_parity(key):
     case = wl.build(key)
     run = gpu_prefill(case)
@@ -348,7 +348,7 @@ def test_fused_rope_workload_full_parity(key):
     assert max_err(got, oracle_prefill(case)) <= ATOL
 
 
-@pytest.mark.parametrize("key", ["2", "3b"])
+@pytest.mark.parametrize("key", ["2", "3b", "3c"])
 def test_fused_rope_workload_sampled_parity(key):
     case = wl.build(key)
     got = gpu_prefill_fused(case).out.cpu().numpy()

@@ -209,6 +209,12 @@ WORKLOADS = {
                    "16 sequences of 2048, 9 q heads / 3 kv heads, causal, theta 1e5",
                    dict(lengths=[2048] * 16, H=9, G=3, packed=False, window=-1, causal=True,
                         theta=100000.0)),
+    # The same layer read as one call: the 1142-token sequence packed with the 16 x 2048 batch.
+    "3c": Workload("3c", "smollm2_causal_gqa_1142_plus_16x2048", 1203, "prefill",
+                   "one 1142-token sequence packed with 16 sequences of 2048 (33910 tokens), "
+                   "9 q heads / 3 kv heads, causal, theta 1e5",
+                   dict(lengths=[1142] + [2048] * 16, H=9, G=3, packed=False, window=-1,
+                        causal=True, theta=100000.0)),
     "4": Workload("4", "smollm2_decode_b64", 1004, "decode",
                   "64 sequences, one new token each, 9 q heads / 3 kv heads, caches "
                   "[64][3][8192][64] f32, used U[1143,8192], theta 1e5",
