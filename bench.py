@@ -97,6 +97,7 @@ def time_calls(torch, fn, steps, warmup, flush=None):
         b.record()
     torch.cuda.synchronize()
     times = [a.elapsed_time(b) for a, b in evs]
+    time_calls.median = float(np.median(times))
     return float(np.mean(times)), float(np.min(times))
 
 
@@ -113,6 +114,7 @@ def prefill_part(torch, key, steps, warmup, flush):
     del out16
     run.rope()
     mean_ms, min_ms = time_calls(torch, run.attention, steps, warmup, flush)
+    median_ms = time_calls.median
     rope_ms, _ = time_calls(torch, run.rope, max(3, steps // 4), 1, flush)
     flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
     tflops = flops / (mean_ms * 1e-3) / 1e12
@@ -120,6 +122,7 @@ def prefill_part(torch, key, steps, warmup, flush):
     res = {"workload": wl.WORKLOADS[key].name, "tokens": case.T, "seqs": case.S,
            "heads": case.H, "kv_heads": case.G, "window": case.window, "causal": case.causal,
            "attn_ms": round(mean_ms, 4), "attn_ms_min": round(min_ms, 4),
+           "attn_ms_median": round(median_ms, 4),
            "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
            "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
            "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
@@ -247,6 +250,33 @@ def measure_ceilings(torch):
     return res
 
 
+def visible_pairs(case, rows):
+    """Keys visible to the given packed rows, summed (per head)."""
+    seq = np.searchsorted(case.cu, rows, side="right") - 1
+    pos = rows - case.cu[seq]
+    n = case.lengths[seq].astype(np.int64)
+    lo = np.zeros_like(n)
+    hi = n - 1
+    if case.causal:
+        hi = np.minimum(hi, pos)
+    if case.window >= 0:
+        hw = case.window // 2
+        lo = np.maximum(lo, pos - hw)
+        hi = np.minimum(hi, pos + hw)
+    return int(np.sum(hi - lo + 1))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s):
     """The oracle, untuned, on random samples of the workload's rows (all heads each),
     repeated until the time budget is spent."""
@@ -257,8 +287,10 @@ def cpu_baseline(case, budget_s):
     n = 256
     spent = 0.0
     done = 0
+    pairs = 0
     while spent < budget_s:
         rows = np.sort(rng.integers(0, case.T, n)).astype(np.int32)
+        pairs += visible_pairs(case, rows)
         t0 = time.perf_counter()
         oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
                                 case.causal, tables=tables, rows=rows, threads=threads)
@@ -268,7 +300,8 @@ def cpu_baseline(case, budget_s):
         per_row = dt / n
         n = int(min(max(1, (budget_s - spent) / max(per_row, 1e-9)), 4 * n, case.T))
     return {"value": round(done / spent / 1e6, 6), "unit": "Mtok/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "fp64_gflops": round(4 * 64 * case.H * pairs / spent / 1e9, 3),
             "sample": f"{done} query rows drawn uniformly (with replacement) from the headline "
                       f"workload, all {case.H} heads each (RoPE, -inf mask, two-pass softmax in "
                       f"FP64), {spent:.1f} s"}
