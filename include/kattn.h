@@ -31,8 +31,8 @@
  *   clamped to [0, T], positions outside the table leave a row unrotated),
  *   but the results are then unspecified.  With KATTN_CHECK=1 in the
  *   environment each call copies its device tables to the host, validates
- *   them and returns KATTN_EBOUNDS on a bad one (synchronous; debugging
- *   only).  KATTN_SPLIT=0 forces the shared-tile prefill kernel, 1 the
+ *   them and returns KATTN_EBOUNDS on a bad one before queueing any work
+ *   (synchronous; debugging only; read on every call).  KATTN_SPLIT=0 forces the shared-tile prefill kernel, 1 the
  *   key-split kernel that small launches get, 4 or 8 that kernel with 4 or 8
  *   waves per work-group, "band" the persistent sliding-window kernel that
  *   packed batches with a half-window of at most 64 and at most 1023
@@ -275,7 +275,8 @@ size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G);
  *   k_cache, v_cache: device float [B][G][cap][64]; row j of kv head g of
  *               sequence b at ((b*G + g)*cap + j)*64 ([argus text.rs]
  *               `KvAppend` layout, stacked over the batch).
- *   used:       device int32[B], 1 <= used[b] <= max_used.
+ *   used:       device int32[B], 1 <= used[b] <= max_used, or 0 for an idle
+ *               slot of a fixed-shape call.
  *   max_used:   host scalar, 1 <= max_used <= cap; sizes the split over keys.
  *   cos, sin:   device float[table_len][32] with table_len >= max_used, or
  *               both NULL when q and k_new are already rotated.

@@ -568,9 +568,9 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
         std::vector<int32_t> h(B);
         if (hipMemcpy(h.data(), used, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess)
             return fail(KATTN_EDEVICE, "%s: KATTN_CHECK copy of used failed", fn);
-        for (int32_t i = 0; i < B; ++i)
-            if (h[i] < 1 || h[i] > max_used)
-                return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [1, max_used=%d]", fn, i, h[i], max_used);
+        for (int32_t i = 0; i < B; ++i)  // 0 is an idle slot of a fixed-shape call
+            if (h[i] < 0 || h[i] > max_used)
+                return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [0, max_used=%d]", fn, i, h[i], max_used);
     }
     const int R = H / G;
     int waves = 0;

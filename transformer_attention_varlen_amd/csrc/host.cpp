@@ -34,11 +34,8 @@ int ok() {
 }
 
 bool debug_checks() {
-    static const bool on = [] {
-        const char* e = std::getenv("KATTN_CHECK");
-        return e != nullptr && std::strcmp(e, "1") == 0;
-    }();
-    return on;
+    const char* e = std::getenv("KATTN_CHECK");  // read on every call, like KATTN_SPLIT
+    return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
 int device_cus() {
