@@ -434,6 +434,16 @@ def main():
         del flush
     out["parts"] = parts
     out["ceilings"] = measure_ceilings(torch) if args.parts != "none" else None
+    if out["ceilings"] is not None:
+        # the same rates against what the library kernels of this GPU reach (besides the
+        # nominal peaks): a large FP32 GEMM for the MFMA-bound parts, a device copy for decode
+        gemm = out["ceilings"]["fp32_gemm_tflops"]
+        copy = out["ceilings"]["hbm_copy_gbs"]
+        for part in parts.values():
+            if "tflops" in part:
+                part["frac_of_measured_fp32_gemm"] = round(part["tflops"] / gemm, 4)
+            if "gbs" in part:
+                part["frac_of_measured_copy"] = round(part["gbs"] / copy, 4)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     else:
