@@ -142,6 +142,7 @@ def decode_part(torch, steps, warmup, flush):
     case = wl.build("4")
     run = DecodeRun(case, rotate=True)
     mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
+    median_ms = time_calls.median
     # a serving loop: steps back to back (no flush), wall clock over all of them, after a few
     # untimed steps of its own (the per-call timing above ends on a drained GPU)
     loop_steps = max(steps, 200)
@@ -164,6 +165,8 @@ def decode_part(torch, steps, warmup, flush):
     res = {"workload": wl.WORKLOADS["4"].name, "seqs": case.B, "heads": case.H,
            "kv_heads": case.G, "cap": case.cap, "sum_used": int(case.used.sum()),
            "decode_ms": round(mean_ms, 4), "decode_ms_min": round(min_ms, 4),
+           "decode_ms_median": round(median_ms, 4),
+           "frac_hbm_best_call": round(nbytes / (min_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "back_to_back_ms": round(loop_ms, 4),
            "back_to_back_frac_hbm": round(nbytes / (loop_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "graph_replay_ms": round(graph_ms, 4),
@@ -181,11 +184,12 @@ def chunk_part(torch, steps, warmup, flush):
     run = ChunkRun(case, rotate=True)
     # every call appends the same chunk at the same rows, so repeated calls do equal work
     mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
+    median_ms = time_calls.median
     flops = metrics.chunk_flops(case.lengths, case.offsets, case.H)
     tflops = flops / (mean_ms * 1e-3) / 1e12
     res = {"workload": wl.WORKLOADS["5"].name, "seqs": case.B, "chunk_tokens": case.T,
            "heads": case.H, "kv_heads": case.G, "cap": case.cap, "max_ctx": case.max_ctx,
-           "ms": round(mean_ms, 4), "ms_min": round(min_ms, 4),
+           "ms": round(mean_ms, 4), "ms_min": round(min_ms, 4), "ms_median": round(median_ms, 4),
            "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
            "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
            "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4)}
