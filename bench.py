@@ -2,26 +2,32 @@
 """Benchmark of the varlen attention hot path on one MI355X.
 
 Prints ONE JSON line.  A step is one pass of the hot path over the headline
-workload (ModernBERT-base local layer: 64 packed sequences of U[16,512]
-tokens, 12 heads, window 128, RoPE theta 1e4), inputs resident in HBM:
-the attention forward with the RoPE step fused into its tile loads
-(kattn_varlen_fwd_rope: the tile planner, then the tile kernel, which rotates
-q and k as it loads them).  The two-pass form of the same step (in-place RoPE
-prologue, then kattn_varlen_fwd) is timed beside it.  The same line carries the other
-workloads of the path, each timed per call with HIP events on the stream it
-runs on and the L2/MALL flushed between calls:
+workload, the ModernBERT-base global layer at long context (8 packed
+sequences of U[4096,8192] tokens, 52277 in all, 12 heads, head width 64,
+full bidirectional attention, RoPE theta 1.6e5), inputs resident in HBM:
+the in-place RoPE prologue (kattn_rope_prologue), then the attention forward
+(kattn_varlen_fwd: the tile planner, then the FP32-MFMA tile kernel).  The
+fused form of the same step (kattn_varlen_fwd_rope, RoPE inside the tile
+loads) is timed beside it.  The same line carries the other workloads of the
+path, each timed per call with HIP events on the stream it runs on and the
+L2/MALL flushed between calls:
 
-  prefill_global_long   ModernBERT global layer, 8 x U[4096,8192]
+  prefill_local_w128    ModernBERT local layer, 64 x U[16,512], window 128
+  prefill_global_long   the headline workload's fused and binary16-output forms
   prefill_causal_1142   SmolLM2 causal GQA prefill, one 1142-token sequence
   prefill_causal_16x2048 SmolLM2 causal GQA prefill, 16 x 2048
+  prefill_causal_1142_plus_16x2048  both in one call
   decode_b64            SmolLM2 decode, 64 sequences, caches [64][3][8192][64]
   chunked_prefill_b16   SmolLM2 prefill continuing from filled caches, 16 chunks
 
 `roofline` is for the headline step's dominant kernel (the attention tile
-kernel): algorithmic FLOPs per launch over its mean launch time.  `traffic`
-comes from rocprofv3 PMC counters taken offline (see profiles/), or null.
-`cpu_baseline` times the FP64 CPU oracle on a bounded random sample of the
-headline workload's rows.
+kernel): algorithmic FLOPs per launch over its mean launch time, from one HIP
+event pair around every timed attention call on the stream it is queued on.
+`traffic` comes from rocprofv3 PMC counters taken offline (profiles/), or is
+null when the kernel source changed since.  `cpu_baseline` times the FP64 CPU
+oracle on a bounded random sample of the headline workload's rows.
+`pages_cpu_context` quotes the CPU figures the pages print (other hardware,
+other work: context, not a target).
 """
 from __future__ import annotations
 
@@ -36,8 +42,8 @@ import numpy as np
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
-HEADLINE = "1"
-PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
+HEADLINE = "2"
+PARTS = {"1": "prefill_local_w128", "2": "prefill_global_long", "3a": "prefill_causal_1142",
          "3b": "prefill_causal_16x2048", "3c": "prefill_causal_1142_plus_16x2048",
          "4": "decode_b64", "5": "chunked_prefill_b16"}
 
@@ -45,11 +51,13 @@ PARTS = {"2": "prefill_global_long", "3a": "prefill_causal_1142",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 200 of each: the timed region is about 25 ms of headline steps, after as long again
-    # at full clock (a few ms of steps run before the clocks ramp measure 10 % slower)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--parts", default="2,3a,3b,3c,4,5",
+    # the timed region is about 0.4 s of headline steps (8.2 ms each)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--preroll-ms", type=float, default=300.0,
+                    help="after the warmup steps, further untimed steps until this much wall "
+                         "time has passed, so the timed steps start at full clock (reported)")
+    ap.add_argument("--parts", default="1,2,3a,3b,3c,4,5",
                     help="comma list of extra workloads to time, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 disables)")
@@ -271,24 +279,47 @@ def visible_pairs(case, rows):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family, model, stepping, and the
+    number of logical CPUs it lists."""
+    info = {}
+    n = 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k == "processor":
+                    n += 1
+                elif k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{info.get('model name', 'unknown')} (family {info.get('cpu family', '?')}, "
+            f"model {info.get('model', '?')}, stepping {info.get('stepping', '?')}; "
+            f"{n} logical CPUs listed)")
+
+
+def oracle_threads():
+    """Threads the oracle runs with: OMP_NUM_THREADS when set (a GPU machine sets it to the CPU
+    share of one GPU), else every CPU the process may use."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(case, budget_s):
     """The oracle, untuned, on random samples of the workload's rows (all heads each),
     repeated until the time budget is spent."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     tables = oracle.rope_tables(case.theta, max(int(case.lengths.max()), 1))
     rng = np.random.default_rng(0)
-    n = 256
+    n = 64
     spent = 0.0
     done = 0
     pairs = 0
@@ -304,11 +335,38 @@ def cpu_baseline(case, budget_s):
         per_row = dt / n
         n = int(min(max(1, (budget_s - spent) / max(per_row, 1e-9)), 4 * n, case.T))
     return {"value": round(done / spent / 1e6, 6), "unit": "Mtok/s", "cores": threads,
-            "kind": "oracle", "cpu_model": cpu_model(),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "fp64_gflops": round(4 * 64 * case.H * pairs / spent / 1e9, 3),
             "sample": f"{done} query rows drawn uniformly (with replacement) from the headline "
                       f"workload, all {case.H} heads each (RoPE, -inf mask, two-pass softmax in "
-                      f"FP64), {spent:.1f} s"}
+                      f"FP64), {spent:.1f} s on {threads} OpenMP threads"}
+
+
+def pages_cpu_context():
+    """The CPU figures the pages print for this method, quoted as context: an unnamed CPU, FP32,
+    the SmolLM2-135M tower at its 1142-token caption prompt.  Other hardware and other work,
+    so no ratio is taken against them."""
+    where = "ffai-argus 0.7.3 src/text.rs"
+    return {
+        "hardware": "unnamed CPU (candle's CPU backend), FP32",
+        "workload": "SmolLM2-135M text tower, 9 q heads / 3 kv heads, head width 64, "
+                    "1142-token caption prompt and the decode steps after it",
+        "masked_fill_ms_per_layer": {"value": 114.13, "gbs": 0.8,
+                                     "what": "writing -inf into the causal upper triangle of "
+                                             "the (9, 1142, 1142) score matrix",
+                                     "cite": f"{where}, module docs, per-layer table"},
+        "scale_ms_per_layer": {"value": 19.39, "cite": f"{where}, module docs, per-layer table"},
+        "softmax_ms_per_layer": {"value": 5.95, "cite": f"{where}, module docs, per-layer table"},
+        "matmul_gflops": {"value": [516, 591], "what": "candle matmuls at the tower's shapes",
+                          "cite": f"{where}, module docs"},
+        "kv_cat_ms_per_decode_token": {"value": 14.0, "mb_per_token": 52.7,
+                                       "what": "recopying both caches at full length for every "
+                                               "decode token, 30 layers",
+                                       "cite": f"{where}, doc comment of KvAppend"},
+        "here": "this library skips the masked tiles (no mask is written), folds the scale "
+                "into q and appends in place; see parts.prefill_causal_1142 (one layer's "
+                "attention at the same shape) and parts.decode_b64",
+    }
 
 
 def main():
@@ -356,36 +414,49 @@ def main():
 
     case = wl.build(HEADLINE)
     run = PrefillRun(case)
-    # warmup, then K timed steps bracketed by synchronisation, and by one pair of events on the
-    # stream the launches (planner, tile kernel) are queued on.  An event pair around every
-    # step would drain the GPU between steps and time that too (7 % on this step).
+    # W warmup steps, then a pre-roll: further untimed steps until --preroll-ms of wall time
+    # has passed, so that the timed steps run at full clock whatever W is
     for _ in range(args.warmup):
-        run.step_fused()
+        run.step()
     torch.cuda.synchronize()
-    ev_a = torch.cuda.Event(enable_timing=True)
-    ev_b = torch.cuda.Event(enable_timing=True)
+    t_pre = time.perf_counter()
+    preroll_steps = 0
+    while (time.perf_counter() - t_pre) * 1e3 < args.preroll_ms:
+        run.step()
+        preroll_steps += 1
+        torch.cuda.synchronize()
+    preroll_ms = (time.perf_counter() - t_pre) * 1e3
+    # K timed steps bracketed by synchronisation.  In each, an event pair on the stream the
+    # launches are queued on (torch's current stream) brackets the attention call (the
+    # planner and the tile kernel); the prologue runs between the pairs.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev_a.record()
-    for _ in range(args.steps):
-        run.step_fused()
-    ev_b.record()
+    for a, b in evs:
+        run.rope()
+        a.record()
+        run.attention()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = ev_a.elapsed_time(ev_b) / args.steps
+    attn_times = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = float(np.mean(attn_times))
     ms_per_step = wall * 1e3 / args.steps
-    # the two-pass form of the same step: in-place RoPE prologue, then attention
+    # the fused form of the same step: RoPE inside the tile loads (q and k read-only)
+    run.reset_inputs()
     for _ in range(2):
-        run.step()
+        run.step_fused()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
-        run.step()
+        run.step_fused()
     torch.cuda.synchronize()
-    two_pass_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-    # the fused step captured once in a HIP graph and replayed back to back
+    fused_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    # the two-pass step captured once in a HIP graph and replayed back to back
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        run.step_fused()
+        run.step()
     for _ in range(2):
         graph.replay()
     torch.cuda.synchronize()
@@ -401,23 +472,28 @@ def main():
 
     out = {
         "metric": "varlen attention Mtok/s + % FP32-MFMA peak; decode KV GB/s (% HBM)",
-        "value": round(value, 3), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(value, 4), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.WORKLOADS[HEADLINE].name, "tokens": case.T, "seqs": case.S,
                    "heads": case.H, "kv_heads": case.G, "head_dim": 64, "window": case.window,
                    "causal": case.causal, "rope_theta": case.theta,
                    "seed": wl.WORKLOADS[HEADLINE].seed,
-                   "step": "attention forward with RoPE fused into the tile loads",
-                   "two_pass_ms_per_step": round(two_pass_ms, 4),
+                   "step": "RoPE prologue (in place on q and k), then the attention forward",
+                   "preroll": {"steps": preroll_steps, "ms": round(preroll_ms, 1)},
+                   "fused_rope_ms_per_step": round(fused_ms, 4),
                    "graph_replay_ms_per_step": round(graph_ms, 4)},
         "roofline": {"bound": "mfma",
-                     "kernel": "band_kernel, fused-RoPE variant (one event pair over the "
-                               "timed steps: per step the sliding-window kernel and the gaps)",
+                     "kernel": "fwd_kernel<1, 4, 64, 0, false> (FP32-MFMA tile kernel) with "
+                               "plan_kernel (about 5 us) ahead of it: one event pair around each "
+                               "timed kattn_varlen_fwd call",
                      "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": traffic_from_profiles(wl.WORKLOADS[HEADLINE].name, "prefill.hip"),
+                     "algorithmic_bytes_per_launch": metrics.prefill_bytes(case.T, case.H,
+                                                                           case.G),
                      "mean_launch_ms": round(attn_ms, 4),
+                     "median_launch_ms": round(float(np.median(attn_times)), 4),
                      "algorithmic_gflop_per_launch": round(flops / 1e9, 4)},
     }
     del run
@@ -430,11 +506,12 @@ def main():
         for k in keys:
             psteps, pwarm = max(5, args.steps // 2), 2
             if k == "4":
-                parts[PARTS[k]] = decode_part(torch, psteps, pwarm, flush)
+                parts[PARTS[k]] = decode_part(torch, max(psteps, 20), pwarm, flush)
             elif k == "5":
                 parts[PARTS[k]] = chunk_part(torch, psteps, pwarm, flush)
             else:
-                parts[PARTS[k]] = prefill_part(torch, k, psteps, pwarm, flush)
+                parts[PARTS[k]] = prefill_part(torch, k, max(3, psteps // 4) if k == "2" else psteps,
+                                               pwarm, flush)
         del flush
     out["parts"] = parts
     out["ceilings"] = measure_ceilings(torch) if args.parts != "none" else None
@@ -443,6 +520,7 @@ def main():
         # nominal peaks): a large FP32 GEMM for the MFMA-bound parts, a device copy for decode
         gemm = out["ceilings"]["fp32_gemm_tflops"]
         copy = out["ceilings"]["hbm_copy_gbs"]
+        out["roofline"]["frac_of_measured_fp32_gemm"] = round(achieved / gemm, 4)
         for part in parts.values():
             if "tflops" in part:
                 part["frac_of_measured_fp32_gemm"] = round(part["tflops"] / gemm, 4)
@@ -452,6 +530,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    out["pages_cpu_context"] = pages_cpu_context()
     print(json.dumps(out), flush=True)
 
 

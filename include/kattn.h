@@ -129,7 +129,14 @@ int kattn_rope_prologue(float* q, int64_t q_stride, int32_t H, float* k, int64_t
                         const float* sin, int32_t table_len, int32_t head_dim,
                         hipStream_t stream);
 
-/* Bytes of device workspace kattn_varlen_fwd needs for this batch shape. */
+/*
+ * Bytes of device workspace kattn_varlen_fwd (and its _rope and _f16 forms)
+ * needs for a batch of S sequences and T rows.  The caller allocates it once
+ * per bucket and passes it to every call, so no call allocates: the scratch
+ * of the pages' CPU backend is likewise sized for the bucket when its plan is
+ * built, and its run path never allocates ([kime-cpu plan.rs] module docs).
+ * The size depends on S and T only (not on the lengths).  0 for S < 0 or T < 0.
+ */
 size_t kattn_varlen_fwd_workspace(int32_t S, int32_t T);
 
 /*
@@ -209,7 +216,8 @@ int kattn_varlen_fwd_f16(void* out, int64_t out_stride, const float* q, int64_t 
                          const float* cos, const float* sin, int32_t table_len, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace kattn_prefill_cached needs for B sequences and T chunk rows. */
+/* Bytes of device workspace kattn_prefill_cached needs for B sequences and T chunk rows
+ * (sized once per bucket, as kattn_varlen_fwd_workspace). */
 size_t kattn_prefill_cached_workspace(int32_t B, int32_t T);
 
 /*
@@ -254,8 +262,14 @@ int kattn_prefill_cached(float* out, int64_t out_stride, const float* q, int64_t
                          const float* cos, const float* sin, int32_t table_len, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace kattn_decode needs for B sequences, H q heads and G kv
- * heads (0 for invalid sizes).  The size does not depend on the cache lengths. */
+/*
+ * Bytes of device workspace kattn_decode needs for B sequences, H q heads and
+ * G kv heads (0 for invalid sizes).  The size does not depend on the cache
+ * lengths, so one workspace sized for a bucket serves every step of a decode
+ * loop and no step allocates (the bucket-sized, allocate-nothing run path of
+ * [kime-cpu plan.rs] module docs; the preallocated cache of [argus text.rs]
+ * `KvAppend`).
+ */
 size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G);
 
 /*

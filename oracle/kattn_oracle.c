@@ -155,6 +155,10 @@ static int check_cu(const int32_t* cu, int32_t S, int32_t T) {
  * mask_mode 1: leave masked columns out of the max, the sum and P.V (the
  *              skip the argus text.rs module docs argue is bit-identical).
  * threads <= 0: the OpenMP default.
+ * The RoPE step comes first, as in the pages' plan (a Rope step, then the
+ * Attention step): every key row is rotated once, in FP64, at its position
+ * inside its sequence, and the scores read those rotated keys.  Queries are
+ * rotated as their rows are visited.
  */
 static int varlen_attention(void* out, int out_f64, int64_t out_stride, const float* q,
                             int64_t q_stride, const float* k, int64_t k_stride, const float* v,
@@ -184,6 +188,20 @@ static int varlen_attention(void* out, int out_f64, int64_t out_stride, const fl
 #else
     (void)threads;
 #endif
+    /* the RoPE step on the keys: krot[(r*G + g)*64 + d] = RoPE(k row r, head g, pos r - cu[s]) */
+    double* krot = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * (size_t)G * HD);
+    if (!krot) return -1;
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < T; ++r) {
+        int32_t a = 0, b = S - 1; /* the last sequence s with cu[s] <= r (empty ones skipped) */
+        while (a < b) {
+            int32_t mid = (a + b + 1) / 2;
+            if (cu[mid] <= r) a = mid; else b = mid - 1;
+        }
+        for (int32_t g = 0; g < G; ++g)
+            rope_head(k + (int64_t)r * k_stride + (int64_t)g * HD, cos_t, sin_t, r - cu[a],
+                      krot + ((int64_t)r * G + g) * HD);
+    }
     int bad = 0;
 #pragma omp parallel
     {
@@ -201,14 +219,13 @@ static int varlen_attention(void* out, int out_f64, int64_t out_stride, const fl
                 int32_t lo = cu[s], n = cu[s + 1] - cu[s], i = r - lo;
                 for (int32_t h = 0; h < H; ++h) {
                     int32_t g = h / R;
-                    double qr[HD], kr[HD];
+                    double qr[HD];
                     rope_head(q + (int64_t)r * q_stride + (int64_t)h * HD, cos_t, sin_t, i, qr);
                     /* scores and the additive mask over every key of the sequence */
                     for (int32_t j = 0; j < n; ++j) {
                         int vis = visible(i, j, window, causal);
                         if (mask_mode == 1 && !vis) continue;
-                        rope_head(k + (int64_t)(lo + j) * k_stride + (int64_t)g * HD, cos_t,
-                                  sin_t, j, kr);
+                        const double* kr = krot + ((int64_t)(lo + j) * G + g) * HD;
                         double dot = 0.0;
                         for (int d = 0; d < HD; ++d) dot += qr[d] * kr[d];
                         double sij = scale * dot;
@@ -250,6 +267,7 @@ static int varlen_attention(void* out, int out_f64, int64_t out_stride, const fl
         free(z);
         free(e);
     }
+    free(krot);
     return bad ? -1 : 0;
 }
 

@@ -23,8 +23,8 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 @pytest.mark.gpu
 def test_short_run_prints_one_json_line_with_the_contract_fields():
     r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "1", "--parts", "4",
-                        "--cpu-seconds", "0.5"], capture_output=True, text=True, timeout=300,
-                       cwd=ROOT)
+                        "--cpu-seconds", "0.5", "--preroll-ms", "50"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, lines
@@ -35,13 +35,19 @@ def test_short_run_prints_one_json_line_with_the_contract_fields():
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["value"] > 0 and d["ms_per_step"] > 0
-    assert d["config"]["workload"] == "modernbert_local_w128"
+    assert d["config"]["workload"] == "modernbert_global_long"
+    assert d["config"]["preroll"]["steps"] >= 1
     roof = d["roofline"]
     assert roof["bound"] == "mfma" and roof["peak"] == 157.3 and roof["unit"] == "TFLOP/s"
     assert 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    # the headline's value and its kernel's time agree: the tile kernel is most of the step
+    assert roof["mean_launch_ms"] < d["ms_per_step"]
     base = d["cpu_baseline"]
     assert base["kind"] == "oracle" and base["value"] > 0 and base["cores"] >= 1
+    ctx = d["pages_cpu_context"]
+    assert ctx["masked_fill_ms_per_layer"]["value"] == 114.13
+    assert ctx["kv_cat_ms_per_decode_token"]["value"] == 14.0
     dec = d["parts"]["decode_b64"]
     assert dec["decode_ms"] > 0 and dec["back_to_back_ms"] > 0
     assert 0 < dec["frac_hbm"] < 1 and 0 < dec["back_to_back_frac_hbm"] < 1

@@ -5,8 +5,9 @@ compared (FP32 arithmetic in any order against one FP64 rounding, N(0,1)
 inputs); rotated q/k and appended cache rows <= 1e-6 (one or two f32
 roundings of values below 8).  Integer and index work (which rows and cache
 rows are written) is checked exactly.  Full-size workloads run in the launch
-configuration the bench times; where the oracle would take minutes, sampled
-rows are compared (the oracle computes rows one by one).
+configuration the bench times and are compared on every element, the global
+layer one sequence per test item so that no item runs long; only the stress
+cases (one 40000-token sequence, 20000 tiny sequences) compare sampled rows.
 """
 import numpy as np
 import pytest
@@ -133,15 +134,55 @@ def _sample_rows(case, n_random, seed):
     return np.array(sorted(r for r in rows if 0 <= r < case.T), np.int32)
 
 
-@pytest.mark.parametrize("key", ["2", "3b", "3c"])
-def test_workload_sampled_parity(key):
-    case = wl.build(key)
-    run = gpu_prefill(case)
-    got = run.out.cpu().numpy()
-    rows = _sample_rows(case, 24, 7)
-    ref = oracle_prefill(case, rows=rows)
-    assert max_err(got[rows], ref) <= ATOL
-    assert np.all(np.isfinite(got))
+@pytest.fixture(scope="module")
+def gated_outputs():
+    """The GPU outputs of a large workload in both forms the bench times -- fused RoPE
+    (kattn_varlen_fwd_rope on unrotated q/k) and two-pass (the in-place prologue, then
+    kattn_varlen_fwd) -- computed once and kept on the host while that workload's items run."""
+    held = {}
+
+    def get(key):
+        if key not in held:
+            held.clear()
+            case = wl.build(key)
+            run = PrefillRun(case)
+            run.step_fused()
+            torch.cuda.synchronize()
+            fused = run.out.cpu().numpy().copy()
+            run.step()
+            torch.cuda.synchronize()
+            two_pass = run.out.cpu().numpy()
+            del run
+            torch.cuda.empty_cache()
+            held[key] = (case, two_pass, fused)
+        return held[key]
+
+    return get
+
+
+# the global layer one sequence per item (each a few tens of seconds of oracle time), the
+# causal batches whole
+GATED_ITEMS = [("2", s) for s in range(8)] + [("3b", None), ("3c", None)]
+
+
+@pytest.mark.parametrize("key,seq", GATED_ITEMS)
+def test_gated_workload_every_element(gated_outputs, key, seq):
+    case, two_pass, fused = gated_outputs(key)
+    if seq is None:
+        rows = None
+        ref = oracle_prefill(case)
+        a, b = two_pass, fused
+    else:
+        assert case.S == 8
+        rows = np.arange(case.cu[seq], case.cu[seq + 1], dtype=np.int32)
+        ref = oracle_prefill(case, rows=rows)
+        a, b = two_pass[rows], fused[rows]
+    print(f"workload {key} rows {'all' if rows is None else f'of sequence {seq}'}: "
+          f"two-pass {max_err(a, ref):.3e}, fused {max_err(b, ref):.3e}", flush=True)
+    assert max_err(a, ref) <= ATOL
+    assert max_err(b, ref) <= ATOL
+    if seq in (None, 0):
+        assert np.all(np.isfinite(two_pass)) and np.all(np.isfinite(fused))
 
 
 # ----------------------------------------------------------------------------- GPU invariants
@@ -246,8 +287,9 @@ def _check_decode(case, rotate):
         assert max_err(gk[b, :, p], kc[b, :, p]) <= ROPE_ATOL
         assert np.array_equal(gv[b, :, p], vc[b, :, p])
         gk[b, :, p] = kc[b, :, p]
-    # every other cache row is untouched
-    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    # every other cache row is untouched (bit for bit, NaN contents included)
+    assert np.array_equal(gk.view(np.uint32), kc.view(np.uint32))
+    assert np.array_equal(gv.view(np.uint32), vc.view(np.uint32))
 
 
 @pytest.mark.parametrize("rotate", [True, False])
@@ -259,6 +301,20 @@ def test_decode_small(rotate, H, G):
 
 def test_decode_full_workload():
     _check_decode(wl.build("4"), rotate=True)
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+def test_decode_ignores_unused_cache_rows_holding_nan(rotate):
+    # The cache rows from used-1 on are write-only to a decode step: row used-1 receives the
+    # new token and the rows past it are never part of the result.  Filled with NaN here (as
+    # torch.empty or a reused block may leave them), they must not reach the output.  Lengths
+    # put the new row at every offset inside a 32-row block and at piece boundaries.
+    lens = [1, 2, 31, 32, 33, 63, 64, 65, 255, 256, 257, 300, 511, 512]
+    case = _decode_case(lens, 9, 3, 520, seed=31)
+    for b, L in enumerate(lens):
+        case.k_cache[b, :, L - 1:] = np.nan
+        case.v_cache[b, :, L - 1:] = np.nan
+    _check_decode(case, rotate)
 
 
 def test_decode_equals_last_causal_row_of_prefill():
@@ -348,15 +404,6 @@ def test_fused_rope_workload_full_parity(key):
     assert max_err(got, oracle_prefill(case)) <= ATOL
 
 
-@pytest.mark.parametrize("key", ["2", "3b", "3c"])
-def test_fused_rope_workload_sampled_parity(key):
-    case = wl.build(key)
-    got = gpu_prefill_fused(case).out.cpu().numpy()
-    rows = _sample_rows(case, 24, 9)
-    assert max_err(got[rows], oracle_prefill(case, rows=rows)) <= ATOL
-    assert np.all(np.isfinite(got))
-
-
 def test_fused_rope_matches_prologue_then_attention():
     case = wl.make_prefill([300, 5, 129], 9, 3, packed=False, causal=True, theta=100000.0, seed=21)
     fused = gpu_prefill_fused(case).out.cpu().numpy()
@@ -432,8 +479,9 @@ def _check_chunk(case, rotate, pad_rows=3):
         assert max_err(gk[b, :, o:o + n], kc[b, :, o:o + n]) <= ROPE_ATOL
         assert np.array_equal(gv[b, :, o:o + n], vc[b, :, o:o + n])
         gk[b, :, o:o + n] = kc[b, :, o:o + n]
-    # every other cache row is untouched
-    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    # every other cache row is untouched (bit for bit, NaN contents included)
+    assert np.array_equal(gk.view(np.uint32), kc.view(np.uint32))
+    assert np.array_equal(gv.view(np.uint32), vc.view(np.uint32))
     # q, k and v are read-only
     assert np.array_equal(run.q.cpu().numpy(), case.q)
     assert np.array_equal(run.k.cpu().numpy(), case.k)
@@ -454,6 +502,10 @@ CHUNK_CASES = [
 @pytest.mark.parametrize("lengths,offsets,H,G,cap", CHUNK_CASES)
 def test_prefill_cached_small_cases(prefill_kernel, rotate, lengths, offsets, H, G, cap):
     case = wl.make_chunked(lengths, offsets, H, G, cap, theta=1e5, seed=500 + H + cap)
+    # cache rows from the chunk's first row on are write-only to the call: NaN must not leak
+    for b, (n, o) in enumerate(zip(lengths, offsets)):
+        case.k_cache[b, :, o:] = np.nan
+        case.v_cache[b, :, o:] = np.nan
     _check_chunk(case, rotate)
 
 

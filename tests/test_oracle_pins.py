@@ -58,6 +58,50 @@ def test_rope_table_within_f32_angle_rounding(theta):
     assert np.max(np.abs(cos - np.cos(wrong))) > 0.1
 
 
+def _angle_is_an_f32_number(cos, sin, theta, p0, p1, ulps=8):
+    """Per table entry (p in [p0, p1), every pair i): is there an f32 number within `ulps` f32
+    steps of the exact angle p * theta^(-i/32) whose cosine and sine, each rounded once to f32,
+    are exactly the stored entries?"""
+    p = np.arange(p0, p1, dtype=np.float64)[:, None]
+    i = np.arange(32, dtype=np.float64)[None, :]
+    exact = p * theta ** (-i / 32.0)
+    up = np.float32(exact)
+    down = up.copy()
+    c, s = cos[p0:p1], sin[p0:p1]
+    hit = (np.float32(np.cos(np.float64(up))) == c) & (np.float32(np.sin(np.float64(up))) == s)
+    for _ in range(ulps):
+        up = np.nextafter(up, np.float32(np.inf))
+        down = np.nextafter(down, np.float32(-np.inf))
+        for a in (up, down):
+            a64 = np.float64(a)
+            hit |= (np.float32(np.cos(a64)) == c) & (np.float32(np.sin(a64)) == s)
+    return hit
+
+
+@pytest.mark.parametrize("theta", [10000.0, 100000.0, 160000.0])
+def test_rope_table_angle_is_rounded_to_f32_before_cos_and_sin(theta):
+    # The CUDA backend page (kime-cuda plan.rs, `rope_tables`) forms the angle as the product
+    # of the f32 position and an f32 inverse frequency, in f32, and only then widens it for
+    # cos and sin.  So every stored pair is cos/sin of some f32 number near the exact angle.
+    # Past position 4096 neighbouring f32 angles are >= 2^-12 rad apart, far more than an f32
+    # rounding of cos or sin, so an angle formed in f64 (not on the f32 grid) fails this.
+    L = 8192
+    cos, sin = oracle.rope_tables(theta, L)
+    assert np.all(_angle_is_an_f32_number(cos, sin, theta, 0, L))
+    # The same check on tables whose angle is left in f64 (the mistake this pin is for): at
+    # angles of 64 rad and more (f32 steps >= 2^-17 rad) almost no entry has an f32 angle that
+    # reproduces it.  (At small angles the two tables agree, so those entries prove nothing.)
+    e = np.float32(np.arange(32, dtype=np.float32) * np.float32(2.0 / 64.0))
+    inv = np.float32(1.0) / np.float32(theta ** np.float64(e))
+    a64 = np.arange(4096, L, dtype=np.float64)[:, None] * np.float64(inv)[None, :]
+    mc = np.zeros((L, 32), np.float32)
+    ms = np.zeros((L, 32), np.float32)
+    mc[4096:], ms[4096:] = np.float32(np.cos(a64)), np.float32(np.sin(a64))
+    hit = _angle_is_an_f32_number(mc, ms, theta, 4096, L)
+    large = a64 >= 64.0
+    assert large.sum() > 4096 and np.mean(hit[large]) < 0.1
+
+
 # ----------------------------------------------------------------------------- RoPE rotation
 
 def _hf_rope(x64, pos, cos, sin):

@@ -281,9 +281,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
             // 1. this block's K and V rows are in kr / vr (loaded before the loop or at the end
             // of the previous trip)
             if (owns_new && base + kBlock > pnew) {  // the block holding the new row
+                // Row pnew and the padding rows after it (loaded clamped to pnew, so they hold
+                // the cache slot's old contents, which may be anything) take the new row.  The
+                // padding rows have weight 0, and 0 * v stays 0 only for a finite v.
 #pragma unroll
                 for (int i = 0; i < kBlock / 4; ++i) {
-                    if (base + 4 * i + grp == pnew) {
+                    if (base + 4 * i + grp >= pnew) {
                         kr[i] = knew;
                         vr[i] = vnew;
                     }

@@ -18,7 +18,7 @@ int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Clears the message (called on every successful entry).
 int ok();
 
-// True when KATTN_CHECK=1 (read once).
+// True when KATTN_CHECK=1 (read on every call, so a test can switch it within a process).
 bool debug_checks();
 
 // Compute units of the current device (cached per device; 256 if the query fails).
