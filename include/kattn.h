@@ -308,6 +308,28 @@ int kattn_decode(float* out, const float* q, const float* k_new, const float* v_
                  float scale, const float* cos, const float* sin, int32_t table_len,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kattn_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same result, with the key-split
+ * partials in a static scratch of 16 MiB that the library holds on every GPU
+ * it runs on until the process ends.  The caller still passes every input
+ * and output.  Arguments and errors as kattn_decode, without `workspace` and
+ * `workspace_bytes`; EBOUNDS when B, H and G need more scratch than 16 MiB
+ * (about (1024 + min(B, 1024) * G) * (H / G) * 264 bytes on a 256-CU GPU:
+ * B = 64, H = 9, G = 3 needs under 1 MiB), EDEVICE when the scratch has no
+ * address on the current GPU.  The call allocates nothing, and nothing in
+ * the scratch needs clearing between calls.  Every call on one GPU shares
+ * that GPU's scratch: two calls that overlap on one GPU (queued on different
+ * streams, or from different threads) race on it and give wrong results;
+ * calls on one stream run one after the other and are safe.
+ */
+int kattn_decode_noalloc(float* out, const float* q, const float* k_new, const float* v_new,
+                         float* k_cache, float* v_cache, int32_t cap, const int32_t* used,
+                         int32_t max_used, int32_t B, int32_t H, int32_t G, int32_t head_dim,
+                         float scale, const float* cos, const float* sin, int32_t table_len,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(kattn.EXPORTS)
     L = kattn.lib()
     for n in names:
@@ -216,6 +216,32 @@ def test_decode_rejects_bad_arguments_on_the_host(kw, code):
 
 def test_decode_empty_batch_queues_nothing():
     assert _dec(B=0, out=None) == kattn.KATTN_OK
+
+
+def _dec_noalloc(**kw):
+    a = dict(out=P(256), q=P(256), k_new=P(256), v_new=P(256), k_cache=P(256), v_cache=P(256),
+             cap=8192, used=P(256), max_used=8000, B=64, H=9, G=3, head_dim=64, scale=0.125,
+             cos=P(256), sin=P(256), table_len=8192, stream=None)
+    a.update(kw)
+    return kattn.lib().kattn_decode_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=80), kattn.KATTN_EUNSUPPORTED),
+    (dict(H=9, G=2), kattn.KATTN_EUNSUPPORTED),
+    (dict(B=-1), kattn.KATTN_EINVAL),
+    (dict(max_used=8193), kattn.KATTN_EBOUNDS),
+    (dict(sin=None), kattn.KATTN_EINVAL),
+    (dict(q=None), kattn.KATTN_EINVAL),
+    (dict(v_new=P(260)), kattn.KATTN_EUNSUPPORTED),
+])
+def test_decode_noalloc_rejects_bad_arguments_on_the_host(kw, code):
+    assert _dec_noalloc(**kw) == code
+    assert b"kattn_decode_noalloc" in kattn.lib().kattn_last_error()
+
+
+def test_decode_noalloc_empty_batch_queues_nothing():
+    assert _dec_noalloc(B=0, out=None) == kattn.KATTN_OK
 
 
 def test_decode_workspace_size():

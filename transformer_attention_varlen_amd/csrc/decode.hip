@@ -507,13 +507,16 @@ int persistent_waves(int R, int* waves) {
     return KATTN_OK;
 }
 
+// Workspace layout for B sequences when a launch runs `waves` persistent waves: the schedule
+// header, then one partial (o[64], then max and sum) per (piece, q head of the group).  A piece
+// id is wave + b * G + g < waves + bs * G, so that many slots per q head suffice.
 struct WsLayout {
     size_t head, part_o, part_ml, total;
 };
-WsLayout ws_layout(int32_t B, int32_t H, int32_t G) {
+WsLayout ws_layout(int32_t B, int32_t H, int32_t G, int waves) {
     const size_t align = 255;
     const int32_t bs = std::min(B, kMaxSeqs);
-    const size_t slots = (static_cast<size_t>(kMaxWaves) + static_cast<size_t>(bs) * G) * (H / G);
+    const size_t slots = (static_cast<size_t>(waves) + static_cast<size_t>(bs) * G) * (H / G);
     WsLayout l;
     l.head = 0;
     l.part_o = ((static_cast<size_t>(kMaxSeqs) + 2) * sizeof(int32_t) + align) & ~align;
@@ -522,6 +525,40 @@ WsLayout ws_layout(int32_t B, int32_t H, int32_t G) {
     return l;
 }
 
+// The allocation-free entry point's scratch: one copy per GPU, held until the process ends,
+// used in place of a caller workspace (the same layout, sized for the waves one launch runs).
+// Host code never passes `scratch` itself to a kernel (on the host it names a shadow
+// variable, not device memory); it passes the device address that hipGetSymbolAddress
+// returns for the current GPU, looked up once per GPU.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+int scratch_address(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KATTN_EDEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr)
+            return KATTN_EDEVICE;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return KATTN_OK;
+}
+
+// The host checks and launches shared by kattn_decode and kattn_decode_noalloc.  With
+// static_scratch the call runs on the current GPU's static scratch (workspace is ignored).
+int decode_call(const char* fn, float* out, const float* q, const float* k_new,
+                const float* v_new, float* k_cache, float* v_cache, int32_t cap,
+                const int32_t* used, int32_t max_used, int32_t B, int32_t H, int32_t G,
+                int32_t head_dim, float scale, const float* cos, const float* sin,
+                int32_t table_len, bool static_scratch, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
 }  // namespace
 }  // namespace kattn
 
@@ -529,7 +566,7 @@ using namespace kattn;
 
 extern "C" size_t kattn_decode_workspace(int32_t B, int32_t H, int32_t G) {
     if (B < 0 || H < 1 || G < 1 || H % G != 0) return 0;
-    return ws_layout(B, H, G).total;
+    return ws_layout(B, H, G, kMaxWaves).total;
 }
 
 extern "C" int kattn_decode(float* out, const float* q, const float* k_new, const float* v_new,
@@ -537,7 +574,31 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
                             int32_t max_used, int32_t B, int32_t H, int32_t G, int32_t head_dim,
                             float scale, const float* cos, const float* sin, int32_t table_len,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "kattn_decode";
+    return decode_call("kattn_decode", out, q, k_new, v_new, k_cache, v_cache, cap, used,
+                       max_used, B, H, G, head_dim, scale, cos, sin, table_len, false, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" int kattn_decode_noalloc(float* out, const float* q, const float* k_new,
+                                    const float* v_new, float* k_cache, float* v_cache,
+                                    int32_t cap, const int32_t* used, int32_t max_used, int32_t B,
+                                    int32_t H, int32_t G, int32_t head_dim, float scale,
+                                    const float* cos, const float* sin, int32_t table_len,
+                                    hipStream_t stream) {
+    return decode_call("kattn_decode_noalloc", out, q, k_new, v_new, k_cache, v_cache, cap, used,
+                       max_used, B, H, G, head_dim, scale, cos, sin, table_len, true, nullptr, 0,
+                       stream);
+}
+
+namespace kattn {
+namespace {
+
+int decode_call(const char* fn, float* out, const float* q, const float* k_new,
+                const float* v_new, float* k_cache, float* v_cache, int32_t cap,
+                const int32_t* used, int32_t max_used, int32_t B, int32_t H, int32_t G,
+                int32_t head_dim, float scale, const float* cos, const float* sin,
+                int32_t table_len, bool static_scratch, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
     if (head_dim != kHeadDim)
         return fail(KATTN_EUNSUPPORTED, "%s: head_dim %d, only 64 is supported", fn, head_dim);
     if (B < 0 || H < 1 || G < 1) return fail(KATTN_EINVAL, "%s: B=%d H=%d G=%d", fn, B, H, G);
@@ -555,32 +616,52 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     if (cos != nullptr && table_len < max_used)
         return fail(KATTN_EBOUNDS, "%s: table_len %d < max_used %d", fn, table_len, max_used);
     if (B == 0) return ok();
-    if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !used || !workspace)
+    if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !used ||
+        (!static_scratch && !workspace))
         return fail(KATTN_EINVAL, "%s: null pointer", fn);
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) ||
         !aligned16(k_cache) || !aligned16(v_cache) || (cos && (!aligned16(cos) || !aligned16(sin))))
         return fail(KATTN_EUNSUPPORTED, "%s: pointers must be multiples of 16 bytes", fn);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
-    const WsLayout lay = ws_layout(B, H, G);
-    if (workspace_bytes < lay.total)
-        return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, lay.total);
+    WsLayout lay{};
+    if (!static_scratch) {
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(KATTN_EUNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+        lay = ws_layout(B, H, G, kMaxWaves);
+        if (workspace_bytes < lay.total)
+            return fail(KATTN_EBOUNDS, "%s: workspace %zu bytes < %zu", fn, workspace_bytes,
+                        lay.total);
+    }
     if (static_cast<int64_t>(max_used) * G * std::min(B, kMaxSeqs) >= 0x7fffffff)
         return fail(KATTN_EBOUNDS, "%s: rows of one launch exceed 2^31", fn);
-    if (debug_checks()) {
-        std::vector<int32_t> h(B);
-        if (hipMemcpy(h.data(), used, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess)
-            return fail(KATTN_EDEVICE, "%s: KATTN_CHECK copy of used failed", fn);
-        for (int32_t i = 0; i < B; ++i)  // 0 is an idle slot of a fixed-shape call
-            if (h[i] < 0 || h[i] > max_used)
-                return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [0, max_used=%d]", fn, i, h[i], max_used);
-    }
     const int R = H / G;
     int waves = 0;
     if (persistent_waves(R, &waves) != KATTN_OK)
         return fail(KATTN_EDEVICE, "%s: occupancy query failed or the kernel does not fit a CU", fn);
     waves -= waves % kWaves;
-
+    if (static_scratch) {
+        // the layout for the waves this GPU's launches run, within the static scratch
+        lay = ws_layout(B, H, G, waves);
+        if (lay.total > kScratchBytes)
+            return fail(KATTN_EBOUNDS,
+                        "%s: B=%d H=%d G=%d needs %zu bytes of scratch, above the %zu-byte static "
+                        "scratch (use kattn_decode with a workspace)",
+                        fn, B, H, G, lay.total, kScratchBytes);
+        if (scratch_address(&workspace) != KATTN_OK)
+            return fail(KATTN_EDEVICE, "%s: the static scratch has no address on this GPU", fn);
+    }
+    if (debug_checks()) {
+        // copied in pieces through a stack buffer, so that the check allocates nothing either
+        int32_t h[256];
+        for (int32_t i0 = 0; i0 < B; i0 += 256) {
+            const int32_t n = std::min<int32_t>(256, B - i0);
+            if (hipMemcpy(h, used + i0, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess)
+                return fail(KATTN_EDEVICE, "%s: KATTN_CHECK copy of used failed", fn);
+            for (int32_t i = 0; i < n; ++i)  // 0 is an idle slot of a fixed-shape call
+                if (h[i] < 0 || h[i] > max_used)
+                    return fail(KATTN_EBOUNDS, "%s: used[%d]=%d outside [0, max_used=%d]", fn,
+                                i0 + i, h[i], max_used);
+        }
+    }
     char* ws = static_cast<char*>(workspace);
     // sequences are taken kMaxSeqs at a time (the schedule's prefix table lives in LDS)
     for (int32_t s0 = 0; s0 < B; s0 += kMaxSeqs) {
@@ -626,3 +707,6 @@ extern "C" int kattn_decode(float* out, const float* q, const float* k_new, cons
     }
     return ok();
 }
+
+}  // namespace
+}  // namespace kattn

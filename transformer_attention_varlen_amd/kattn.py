@@ -31,7 +31,7 @@ KATTN_EDEVICE = -4
 EXPORTS = ("kattn_last_error", "kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
            "kattn_varlen_fwd_workspace", "kattn_varlen_fwd", "kattn_varlen_fwd_rope",
            "kattn_varlen_fwd_f16", "kattn_prefill_cached_workspace", "kattn_prefill_cached",
-           "kattn_decode_workspace", "kattn_decode")
+           "kattn_decode_workspace", "kattn_decode", "kattn_decode_noalloc")
 
 
 class KattnError(RuntimeError):
@@ -74,9 +74,11 @@ def lib():
         L.kattn_decode_workspace.restype = sz
         L.kattn_decode.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, f32, p, p,
                                    i32, p, sz, p]
+        L.kattn_decode_noalloc.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, f32,
+                                           p, p, i32, p]
         for name in ("kattn_rope_tables", "kattn_build_index", "kattn_rope_prologue",
                      "kattn_varlen_fwd", "kattn_varlen_fwd_rope", "kattn_varlen_fwd_f16",
-                     "kattn_prefill_cached", "kattn_decode"):
+                     "kattn_prefill_cached", "kattn_decode", "kattn_decode_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -327,3 +329,16 @@ def kattn_decode(out, q, k_new, v_new, k_cache, v_cache, cap: int, used, max_use
                               _dev(v_cache), cap, _dev(used), max_used, B, H, G, HEAD_DIM,
                               float(scale), _dev(cos), _dev(sin), table_len, _dev(workspace),
                               ws_bytes, _stream(stream)))
+
+
+def kattn_decode_noalloc(out, q, k_new, v_new, k_cache, v_cache, cap: int, used, max_used: int,
+                         B: int, H: int, G: int, *, scale: float = 0.125, cos=None, sin=None,
+                         stream=None):
+    """kattn_decode on the library's static per-GPU scratch: no workspace, nothing allocated."""
+    fn = "kattn_decode_noalloc"
+    _decode_operands(fn, out, q, k_new, v_new, k_cache, v_cache, cap, used, B, H, G)
+    table_len = _tables(fn, cos, sin, 1, required=False)
+    _check(lib().kattn_decode_noalloc(_dev(out), _dev(q), _dev(k_new), _dev(v_new), _dev(k_cache),
+                                      _dev(v_cache), cap, _dev(used), max_used, B, H, G, HEAD_DIM,
+                                      float(scale), _dev(cos), _dev(sin), table_len,
+                                      _stream(stream)))
