@@ -138,7 +138,8 @@ def prefill_part(torch, key, steps, warmup, flush):
            "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1),
            "fused_rope_attn_ms": round(fused_ms, 4),
            "fused_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-           "fused_f16_out_ms": round(f16_ms, 4)}
+           "fused_f16_out_ms": round(f16_ms, 4),
+           "traffic": part_traffic(wl.WORKLOADS[key].name, "prefill.hip")}
     del run
     torch.cuda.empty_cache()
     return res
@@ -179,7 +180,8 @@ def decode_part(torch, steps, warmup, flush):
            "back_to_back_frac_hbm": round(nbytes / (loop_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "graph_replay_ms": round(graph_ms, 4),
            "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
-           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+           "traffic": part_traffic(wl.WORKLOADS["4"].name, "decode.hip")}
     del run
     torch.cuda.empty_cache()
     return res
@@ -206,9 +208,10 @@ def chunk_part(torch, steps, warmup, flush):
     return res
 
 
-def traffic_from_profiles(workload: str, kernel_source: str):
-    """HBM bytes per launch measured with rocprofv3 PMC counters (profiles/traffic.json), or
-    None when the kernel source has changed since they were taken."""
+def traffic_record(workload: str, kernel_source: str):
+    """The rocprofv3 PMC record of a workload's dominant kernel (profiles/traffic.json: HBM
+    bytes fetched and written per launch, scaled by a copy of known size), or None when there
+    is none or the kernel source has changed since the counters were taken."""
     import hashlib
     from pathlib import Path
     root = Path(__file__).resolve().parent
@@ -219,7 +222,22 @@ def traffic_from_profiles(workload: str, kernel_source: str):
     src = root / "transformer_attention_varlen_amd" / "csrc" / kernel_source
     if hashlib.sha256(src.read_bytes()).hexdigest() != rec.get("source_sha256"):
         return None
-    return rec["traffic_bytes"]
+    return rec
+
+
+def traffic_from_profiles(workload: str, kernel_source: str):
+    """HBM bytes per launch (PMC), or None (see traffic_record)."""
+    rec = traffic_record(workload, kernel_source)
+    return None if rec is None else rec["traffic_bytes"]
+
+
+def part_traffic(workload: str, kernel_source: str):
+    """The PMC traffic of a part's kernel, with the kernel (and form) it was measured on."""
+    rec = traffic_record(workload, kernel_source)
+    if rec is None:
+        return None
+    return {"bytes_per_launch": rec["traffic_bytes"], "fetch": rec["fetch_bytes"],
+            "write": rec["write_bytes"], "kernel": rec["kernel"]}
 
 
 def measure_ceilings(torch):
