@@ -163,6 +163,22 @@ def decode_part(torch, steps, warmup, flush):
         run.step()
     torch.cuda.synchronize()
     loop_ms = (time.perf_counter() - t) * 1e3 / loop_steps
+    # per call with the caches flushed before it, without an event pair around it: a loop of
+    # (flush, step) pairs less a loop of flushes alone, both queued with no host wait inside
+    # (the flush reads 1 GiB, so the host stays ahead of the GPU)
+    n_fl = max(steps, 100)
+
+    def loop_wall(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_fl):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n_fl
+
+    pair_ms = loop_wall(lambda: (flush(), run.step()))
+    flush_ms = loop_wall(flush)
+    flushed_ms = pair_ms - flush_ms
     # the same step captured once in a HIP graph and replayed (fixed shape, device counts)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -178,6 +194,9 @@ def decode_part(torch, steps, warmup, flush):
            "frac_hbm_best_call": round(nbytes / (min_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "back_to_back_ms": round(loop_ms, 4),
            "back_to_back_frac_hbm": round(nbytes / (loop_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "flushed_loop_ms": round(flushed_ms, 4),
+           "flushed_loop_frac_hbm": round(nbytes / (flushed_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "flushed_loop_how": f"{n_fl} (flush, step) pairs less {n_fl} flushes, wall clock",
            "graph_replay_ms": round(graph_ms, 4),
            "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),

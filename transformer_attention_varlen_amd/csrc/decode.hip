@@ -17,7 +17,10 @@
 //   leaves one partial per piece; the combine kernel merges the pieces.
 //   Rows are read 4 per 16-byte load instruction (16 lanes per 256-byte
 //   row), so each instruction reads 1 KB of contiguous cache, through the
-//   nontemporal load path (each row is read once per step).
+//   nontemporal load path (each row is read once per step).  A block's rows
+//   are requested as soon as the previous block's K rows are in LDS, so a
+//   wave's loads overlap its scoring of the previous block (V alternates
+//   between two register buffers).
 // * Per block of 32 rows the K rows go through LDS (XOR-swizzled 16-byte
 //   chunks, conflict-free both ways) so that each lane then scores one row:
 //   the softmax math (max, exp, sum) runs once per row instead of once per
@@ -237,16 +240,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
         const float4* kb = reinterpret_cast<const float4*>(p.k_cache + head_off * 64) + t;
         const float4* vb = reinterpret_cast<const float4*>(p.v_cache + head_off * 64) + t;
 
-        // K and V rows base + 4i + grp of a block (clamped: always in bounds; extras are masked)
-        float4 kr[kBlock / 4], vr[kBlock / 4];
-#define KATTN_BLOCK_LOADS(BASE)                                                 \
-    _Pragma("unroll") for (int i = 0; i < kBlock / 4; ++i) {                    \
-        const int rr = min((BASE) + 4 * i + grp, c1 - 1);                       \
-        kr[i] = load_stream(kb + static_cast<int64_t>(rr) * 16);                \
-        vr[i] = load_stream(vb + static_cast<int64_t>(rr) * 16);                \
-    }
+        // K and V rows base + 4i + grp of a block (clamped: always in bounds; extras are masked).
+        // A block's rows are requested as soon as the previous block's K rows are staged in LDS,
+        // so their latency overlaps that block's scores, softmax and P.V; V is double-buffered
+        // (the P.V reads one buffer while the next block's rows fill the other).
+        float4 kr[kBlock / 4], vA[kBlock / 4], vB[kBlock / 4];
+        auto block_loads = [&](int base0, float4 (&vdst)[kBlock / 4]) {
+#pragma unroll
+            for (int i = 0; i < kBlock / 4; ++i) {
+                const int rr = min(base0 + 4 * i + grp, c1 - 1);
+                kr[i] = load_stream(kb + static_cast<int64_t>(rr) * 16);
+                vdst[i] = load_stream(vb + static_cast<int64_t>(rr) * 16);
+            }
+        };
         // the first block's loads go out before the q work, so the two latencies overlap
-        KATTN_BLOCK_LOADS(c0)
+        block_loads(c0, vA);
 
         wave_sync();  // the previous piece is done with Qs
         for (int u = grp; u < R; u += 4) {
@@ -277,13 +285,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
             o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
 
-        for (int base = c0; base < c1; base += kBlock) {
-            // 1. this block's K and V rows are in kr / vr (loaded before the loop or at the end
-            // of the previous trip)
-            if (owns_new && base + kBlock > pnew) {  // the block holding the new row
-                // Row pnew and the padding rows after it (loaded clamped to pnew, so they hold
-                // the cache slot's old contents, which may be anything) take the new row.  The
-                // padding rows have weight 0, and 0 * v stays 0 only for a finite v.
+        // One block of 32 rows: its K rows are in kr and its V rows in vr; the next block's
+        // rows are requested into kr and vnext once this block's K rows are in LDS.
+        auto block_step = [&](int base, float4 (&vr)[kBlock / 4], float4 (&vnext)[kBlock / 4]) {
+            // 1. the block holding the new row: row pnew and the padding rows after it (loaded
+            // clamped to pnew, so they hold the cache slot's old contents, which may be
+            // anything) take the new row.  The padding rows have weight 0, and 0 * v stays 0
+            // only for a finite v.
+            if (owns_new && base + kBlock > pnew) {
 #pragma unroll
                 for (int i = 0; i < kBlock / 4; ++i) {
                     if (base + 4 * i + grp >= pnew) {
@@ -299,6 +308,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
                 *reinterpret_cast<float4*>(&Ks[row * 64 + 4 * (t ^ (row & 15))]) = kr[i];
             }
             wave_sync();
+            if (base + kBlock < c1) block_loads(base + kBlock, vnext);
 
             // 2. scores: lane (hf, j) dots row j over dims 32hf..32hf+31, halves then summed.
             // q is read from LDS each block: an opaque offset keeps the compiler from hoisting
@@ -357,11 +367,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecParams p) 
                 }
                 o[u] = acc;
             }
-            if (base + kBlock < c1) {
-                KATTN_BLOCK_LOADS(base + kBlock)
-            }
+        };
+        // two blocks per trip, so the V buffers swap roles without register copies
+        for (int base = c0; base < c1; base += 2 * kBlock) {
+            block_step(base, vA, vB);
+            if (base + kBlock < c1) block_step(base + kBlock, vB, vA);
         }
-#undef KATTN_BLOCK_LOADS
 
         // the piece's partials: max (uniform), sum over the rows, output summed over the groups
         const int64_t piece = static_cast<int64_t>(w) + static_cast<int64_t>(b) * p.G + g;
@@ -480,8 +491,8 @@ const void* split_kernel_for(int R) {
 }
 
 // Waves of the persistent split grid on the current device: one 4-wave work-group per CU
-// (cached per device and R).  With the nontemporal loads one work-group per CU (one wave per
-// SIMD) streams faster than the 3 the registers would allow (83 against 88 us on the b64
+// (cached per device and R).  With the loads of the next block issued during the current
+// one, two work-groups per CU stream no faster (76.1-76.4 against 76.2-76.5 us on the b64
 // decode), and fewer, longer ranges leave fewer pieces to merge.  EDEVICE when the device
 // cannot hold one work-group of the kernel per CU.
 int persistent_waves(int R, int* waves) {
