@@ -320,7 +320,7 @@ __host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16
 // tile_scores is the part up to the P.V product (scores, mask, running max and sum, rescale of
 // O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue loads between
 // the two.
-template <bool TWO>
+template <bool TWO, bool SKIP = TWO>
 __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
                                             f32x16& S1, f32x16& O0, f32x16& O1, float& m_run,
                                             float& l_run, bool full, int kt, KeyInterval vis,
@@ -391,10 +391,11 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
         }
     }
     l_run = l_run * alpha + psum;
-    // With 64-key tiles (long global and causal rows) the running max rarely moves after the
-    // first tiles: the rescale is skipped when it moved in no lane (alpha is then exactly 1, so
-    // the result is unchanged).  On 32-key tiles the test measured slower than the multiplies.
-    if (!TWO || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    // SKIP: over long key ranges (64-key tiles of global and causal rows, the key-split kernel's
+    // runs) the running max rarely moves after the first tiles, so the rescale is skipped when it
+    // moved in no lane (alpha is then exactly 1, so the result is unchanged).  On the short
+    // rows of a sliding window the test measured slower than the multiplies.
+    if (!SKIP || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             O0[r] *= alpha;
@@ -605,19 +606,46 @@ void fwd_kernel(FwdParams p) {
     // With ROPE_K each K row also brings cos and sin of its four pairs (its position is its
     // key index).
     v4 pt[2 * ROWS];
-#define KATTN_FETCH(K0)                                                                         \
-    _Pragma("unroll") for (int i = 0; i < ROWS; ++i) {                                          \
-        const int64_t r = min((K0) + srow + rstep * i, nk - 1);                                 \
-        const v4* krow = reinterpret_cast<const v4*>(kbase + r * p.k_stride);                   \
-        const v4* vrow = reinterpret_cast<const v4*>(vbase + r * p.v_stride);                   \
-        pk[2 * i] = krow[schunk];                                                               \
-        pk[2 * i + 1] = krow[schunk + 8];                                                       \
-        pv[2 * i] = vrow[schunk];                                                               \
-        pv[2 * i + 1] = vrow[schunk + 8];                                                       \
+    // Row addresses: a tile that lies inside the keys starts at a wave-uniform address (scalar
+    // arithmetic) and each thread adds its fixed row offsets, so no row costs a 64-bit multiply
+    // on the vector ALU (which the FP32 MFMA shares: global layer 8086 -> 8048 us, causal
+    // 16x2048 647.7 -> 645.0 us).  A tile that runs past the last key clamps each row to it
+    // instead, as does every tile of the fused-rotation form (measured 0.3 % slower the other
+    // way).
+    const int64_t koff0 = static_cast<int64_t>(srow) * p.k_stride;
+    const int64_t voff0 = static_cast<int64_t>(srow) * p.v_stride;
+    const int64_t kstep = static_cast<int64_t>(rstep) * p.k_stride;
+    const int64_t vstep = static_cast<int64_t>(rstep) * p.v_stride;
+#define KATTN_FETCH_ROW(KROW, VROW, I, R)                                                       \
+    {                                                                                           \
+        pk[2 * (I)] = (KROW)[schunk];                                                           \
+        pk[2 * (I) + 1] = (KROW)[schunk + 8];                                                   \
+        pv[2 * (I)] = (VROW)[schunk];                                                           \
+        pv[2 * (I) + 1] = (VROW)[schunk + 8];                                                   \
         if constexpr (ROPE_K) {                                                                 \
-            const int64_t trow = min(r, static_cast<int64_t>(p.table_len) - 1) * 32;           \
-            pt[2 * i] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                    \
-            pt[2 * i + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];                \
+            const int64_t trow = min((R), p.table_len - 1) * 32;                                \
+            pt[2 * (I)] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                  \
+            pt[2 * (I) + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];              \
+        }                                                                                       \
+    }
+#define KATTN_FETCH(K0)                                                                         \
+    {                                                                                           \
+        const int k0_ = (K0);                                                                   \
+        if (!ROPE_K && k0_ + TBN <= nk) {                                                       \
+            const float* kt_ = kbase + static_cast<int64_t>(k0_) * p.k_stride;                  \
+            const float* vt_ = vbase + static_cast<int64_t>(k0_) * p.v_stride;                  \
+            _Pragma("unroll") for (int i = 0; i < ROWS; ++i) {                                  \
+                const v4* krow = reinterpret_cast<const v4*>(kt_ + koff0 + i * kstep);          \
+                const v4* vrow = reinterpret_cast<const v4*>(vt_ + voff0 + i * vstep);          \
+                KATTN_FETCH_ROW(krow, vrow, i, k0_ + srow + rstep * i)                          \
+            }                                                                                   \
+        } else {                                                                                \
+            _Pragma("unroll") for (int i = 0; i < ROWS; ++i) {                                  \
+                const int r = min(k0_ + srow + rstep * i, nk - 1);                              \
+                const v4* krow = reinterpret_cast<const v4*>(kbase + static_cast<int64_t>(r) * p.k_stride); \
+                const v4* vrow = reinterpret_cast<const v4*>(vbase + static_cast<int64_t>(r) * p.v_stride); \
+                KATTN_FETCH_ROW(krow, vrow, i, r)                                               \
+            }                                                                                   \
         }                                                                                       \
     }
     // rotate the staged K rows' pairs, x[i] c - x[i+32] s and x[i+32] c + x[i] s, then write K
@@ -673,6 +701,7 @@ void fwd_kernel(FwdParams p) {
         __syncthreads();
     }
 #undef KATTN_FETCH
+#undef KATTN_FETCH_ROW
 #undef KATTN_STASH
 
     const float l_tot = halves_sum(l_run);
@@ -777,19 +806,44 @@ void fwd_split_kernel(FwdParams p) {
     const int srow = lane >> 3, schunk = lane & 7;
     constexpr int kRows = TBN / 8;
     v4 pk[2 * kRows], pv[2 * kRows], pt[2 * kRows];
-#define KATTN_SPLIT_FETCH(K0)                                                                    \
-    _Pragma("unroll") for (int i = 0; i < kRows; ++i) {                                          \
-        const int64_t r = min((K0) + srow + 8 * i, nk - 1);                                      \
-        const v4* krow = reinterpret_cast<const v4*>(kbase + r * p.k_stride);                    \
-        const v4* vrow = reinterpret_cast<const v4*>(vbase + r * p.v_stride);                    \
-        pk[2 * i] = krow[schunk];                                                                \
-        pk[2 * i + 1] = krow[schunk + 8];                                                        \
-        pv[2 * i] = vrow[schunk];                                                                \
-        pv[2 * i + 1] = vrow[schunk + 8];                                                        \
+    // Row addresses as in fwd_kernel: a tile inside the keys from its wave-uniform start plus
+    // this lane's fixed offsets (no per-row 64-bit multiply on the vector ALU); a tile past the
+    // last key clamps each row to it.  With the rescale skip below, the 1142-token causal case
+    // went 29.8 -> 29.4 us.
+    const int64_t koff0 = static_cast<int64_t>(srow) * p.k_stride;
+    const int64_t voff0 = static_cast<int64_t>(srow) * p.v_stride;
+    const int64_t kstep = 8 * p.k_stride;
+    const int64_t vstep = 8 * p.v_stride;
+#define KATTN_SPLIT_FETCH_ROW(KROW, VROW, I, R)                                                  \
+    {                                                                                            \
+        pk[2 * (I)] = (KROW)[schunk];                                                            \
+        pk[2 * (I) + 1] = (KROW)[schunk + 8];                                                    \
+        pv[2 * (I)] = (VROW)[schunk];                                                            \
+        pv[2 * (I) + 1] = (VROW)[schunk + 8];                                                    \
         if constexpr (ROPE_K) {                                                                  \
-            const int64_t trow = min(r, static_cast<int64_t>(p.table_len) - 1) * 32;            \
-            pt[2 * i] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                     \
-            pt[2 * i + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];                 \
+            const int64_t trow = min((R), p.table_len - 1) * 32;                                 \
+            pt[2 * (I)] = reinterpret_cast<const v4*>(p.cos_t + trow)[schunk];                   \
+            pt[2 * (I) + 1] = reinterpret_cast<const v4*>(p.sin_t + trow)[schunk];               \
+        }                                                                                        \
+    }
+#define KATTN_SPLIT_FETCH(K0)                                                                    \
+    {                                                                                            \
+        const int k0_ = (K0);                                                                    \
+        if (k0_ + TBN <= nk) {                                                                   \
+            const float* kt_ = kbase + static_cast<int64_t>(k0_) * p.k_stride;                   \
+            const float* vt_ = vbase + static_cast<int64_t>(k0_) * p.v_stride;                   \
+            _Pragma("unroll") for (int i = 0; i < kRows; ++i) {                                  \
+                const v4* krow = reinterpret_cast<const v4*>(kt_ + koff0 + i * kstep);           \
+                const v4* vrow = reinterpret_cast<const v4*>(vt_ + voff0 + i * vstep);           \
+                KATTN_SPLIT_FETCH_ROW(krow, vrow, i, k0_ + srow + 8 * i)                         \
+            }                                                                                    \
+        } else {                                                                                 \
+            _Pragma("unroll") for (int i = 0; i < kRows; ++i) {                                  \
+                const int r = min(k0_ + srow + 8 * i, nk - 1);                                   \
+                const v4* krow = reinterpret_cast<const v4*>(kbase + static_cast<int64_t>(r) * p.k_stride); \
+                const v4* vrow = reinterpret_cast<const v4*>(vbase + static_cast<int64_t>(r) * p.v_stride); \
+                KATTN_SPLIT_FETCH_ROW(krow, vrow, i, r)                                          \
+            }                                                                                    \
         }                                                                                        \
     }
 #define KATTN_SPLIT_STASH()                                                                      \
@@ -837,7 +891,8 @@ void fwd_split_kernel(FwdParams p) {
         }
         // the next tile's rows are requested between the scores and the P.V product
         f32x16 S0, S1;
-        if (any) tile_scores<false>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        if (any)
+            tile_scores<false, true>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
         if (kt + TBN < t1) {
             KATTN_SPLIT_FETCH(kt + TBN)
         }
@@ -849,6 +904,7 @@ void fwd_split_kernel(FwdParams p) {
         }
     }
 #undef KATTN_SPLIT_FETCH
+#undef KATTN_SPLIT_FETCH_ROW
 #undef KATTN_SPLIT_STASH
 
     // merge the W partial results through LDS
