@@ -46,28 +46,29 @@
 #define HALF (HD / 2)  /* rotated pairs per head */
 
 /*
- * cos/sin tables [len][32] for one RoPE base, rounded the way the CUDA
- * backend page's `rope_tables` does it:
- *   e_i   = (2i)/64 in f32,
- *   inv_i = 1 / f32(theta^e_i computed in f64)        (f32 division),
- *   a     = f64(f32(p) * inv_i)                         (f32 product),
- *   cos, sin of a in f64, rounded to f32.
- * The page says the tables match the CPU backend's.
+ * cos/sin tables [len][32] for one RoPE base.  Reading R5 of the CUDA backend
+ * page's `rope_tables` (which that page says matches the CPU backend):
+ *   - the inverse frequency of pair i is the f32 reciprocal of theta^(i/32),
+ *     the power evaluated in double and rounded to f32 (i/32 is exact in
+ *     binary, so the exponent carries no rounding);
+ *   - the angle at position p is p times that inverse frequency, formed in
+ *     f32 (p itself is exact in f32);
+ *   - the table entries are the cosine and sine of that f32 angle, evaluated
+ *     in double and rounded to f32.
  */
+static float inverse_frequency(double theta, int i) {
+    const float power = (float)pow(theta, (double)i / HALF);
+    return 1.0f / power;
+}
+
 int oracle_rope_tables(double theta, int32_t len, float* cos_out, float* sin_out) {
     if (len < 0 || !(theta > 0.0) || (len > 0 && (!cos_out || !sin_out))) return -1;
-    float inv[HALF];
     for (int i = 0; i < HALF; ++i) {
-        float e = (float)(2 * i) / (float)HD;
-        float pw = (float)pow(theta, (double)e);
-        inv[i] = 1.0f / pw;
-    }
-    for (int32_t p = 0; p < len; ++p) {
-        for (int i = 0; i < HALF; ++i) {
-            float af = (float)p * inv[i];
-            double a = (double)af;
-            cos_out[(int64_t)p * HALF + i] = (float)cos(a);
-            sin_out[(int64_t)p * HALF + i] = (float)sin(a);
+        const float freq = inverse_frequency(theta, i);
+        for (int32_t p = 0; p < len; ++p) {
+            const float angle = (float)p * freq;
+            cos_out[(int64_t)p * HALF + i] = (float)cos((double)angle);
+            sin_out[(int64_t)p * HALF + i] = (float)sin((double)angle);
         }
     }
     return 0;

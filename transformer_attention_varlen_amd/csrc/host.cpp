@@ -75,31 +75,27 @@ using namespace kattn;
 
 extern "C" const char* kattn_last_error(void) { return g_error.c_str(); }
 
-// RoPE tables for heads of 64, rounded as the kime-cuda plan.rs page's
-// `rope_tables` does (which that page ties to the CPU backend).  Each step
-// is its own rounding: the f32 exponent, the f64 power narrowed to f32, the
-// f32 reciprocal, the f32 angle, then cos/sin in f64 narrowed to f32.
+// RoPE tables for heads of 64 (the rounding of the kime-cuda plan.rs page's `rope_tables`,
+// which that page ties to the CPU backend).  Position p and pair i: the angle is the f32 product
+// of p and the pair's inverse frequency, itself the f32 reciprocal of theta^(i/32) evaluated in
+// double and rounded to f32; the entries are that angle's cosine and sine in double, each
+// rounded to f32.  Filled position by position, so each output row is written once.
 extern "C" int kattn_rope_tables(double theta, int32_t len, float* cos_host, float* sin_host) {
     if (!(theta > 0.0) || !std::isfinite(theta))
         return fail(KATTN_EINVAL, "kattn_rope_tables: theta must be finite and > 0 (got %g)", theta);
     if (len < 0) return fail(KATTN_EINVAL, "kattn_rope_tables: len < 0 (%d)", len);
     if (len > 0 && (cos_host == nullptr || sin_host == nullptr))
         return fail(KATTN_EINVAL, "kattn_rope_tables: null output");
-    constexpr int half = kHeadDim / 2;
-    float freq[half];
-    for (int i = 0; i < half; ++i) {
-        const float expo = static_cast<float>(2 * i) / static_cast<float>(kHeadDim);
-        const float base_pow = static_cast<float>(std::pow(theta, static_cast<double>(expo)));
-        freq[i] = 1.0f / base_pow;
-    }
+    constexpr int pairs = kHeadDim / 2;
+    float inv_freq[pairs];
+    for (int i = 0; i < pairs; ++i)
+        inv_freq[i] = 1.0f / static_cast<float>(std::pow(theta, static_cast<double>(i) / pairs));
     for (int32_t p = 0; p < len; ++p) {
-        const float pf = static_cast<float>(p);
-        float* c = cos_host + static_cast<int64_t>(p) * half;
-        float* s = sin_host + static_cast<int64_t>(p) * half;
-        for (int i = 0; i < half; ++i) {
-            const double angle = static_cast<double>(pf * freq[i]);
-            c[i] = static_cast<float>(std::cos(angle));
-            s[i] = static_cast<float>(std::sin(angle));
+        const float pos = static_cast<float>(p);
+        for (int i = 0; i < pairs; ++i) {
+            const float angle = pos * inv_freq[i];
+            cos_host[static_cast<int64_t>(p) * pairs + i] = static_cast<float>(std::cos(static_cast<double>(angle)));
+            sin_host[static_cast<int64_t>(p) * pairs + i] = static_cast<float>(std::sin(static_cast<double>(angle)));
         }
     }
     return ok();
