@@ -447,6 +447,15 @@ __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
 // The Q slice of one lane: dims 16hh .. 16hh+15 and 32+16hh .. 32+16hh+15 of the query in
 // packed row `row` (contraction order, dim_group), times scale; rotated at position pq first
 // when ROT != 0 (in-lane: the slice holds both members of each pair); zeros when !live.
+// One RoPE pair (x[i], x[i+32]) rotated by the angle whose cosine and sine are c and s, times
+// scale.  Every kernel that rotates q goes through this one expression, so the contraction (and
+// the bits) of a rotated q element are the same in all of them.
+__device__ __forceinline__ void rope_pair_scaled(float lo, float hi, float c, float s, float scale,
+                                                 float& out_lo, float& out_hi) {
+    out_lo = (lo * c - hi * s) * scale;
+    out_hi = (hi * c + lo * s) * scale;
+}
+
 template <int ROT>
 __device__ __forceinline__ void load_q(float (&qreg)[32], const FwdParams& p, int64_t row,
                                        int head, int pq, int hh, bool live) {
@@ -474,10 +483,9 @@ __device__ __forceinline__ void load_q(float (&qreg)[32], const FwdParams& p, in
                 const float cs[4] = {ca[m].x, ca[m].y, ca[m].z, ca[m].w};
                 const float sn[4] = {sa[m].x, sa[m].y, sa[m].z, sa[m].w};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    qreg[4 * m + c] = (lo[c] * cs[c] - hi[c] * sn[c]) * p.scale;
-                    qreg[16 + 4 * m + c] = (hi[c] * cs[c] + lo[c] * sn[c]) * p.scale;
-                }
+                for (int c = 0; c < 4; ++c)
+                    rope_pair_scaled(lo[c], hi[c], cs[c], sn[c], p.scale, qreg[4 * m + c],
+                                     qreg[16 + 4 * m + c]);
             }
         } else {
 #pragma unroll
@@ -491,6 +499,57 @@ __device__ __forceinline__ void load_q(float (&qreg)[32], const FwdParams& p, in
     } else {
 #pragma unroll
         for (int m = 0; m < 32; ++m) qreg[m] = 0.0f;
+    }
+}
+
+// The 32 query rows q0 .. q0+31 of one head, loaded once for a whole work-group of NT threads
+// into Qs (row stride LDS_STRIDE): work item (r, c), c < 8, reads dims 4c..4c+3 and their pair
+// members 32+4c..32+4c+3 of row r (16 bytes each, 16 work items per 256-byte row), rotates them
+// at position pos0 + r when ROT != 0 and scales them, with the same arithmetic as load_q.  Rows
+// from nrows on are zeros.  The caller synchronises the work-group before reading Qs; a lane
+// then reads its slice in contraction order (read_q).
+template <int ROT, int NT>
+__device__ __forceinline__ void stage_q(float* Qs, const FwdParams& p, int64_t row0, int head,
+                                        int pos0, int nrows) {
+    for (int it = threadIdx.x; it < 32 * 8; it += NT) {
+        const int r = it >> 3, c = it & 7;
+        float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < nrows) {
+            const float* qrow = p.q + (row0 + r) * p.q_stride + head * kHeadDim;
+            const float4 lo = *reinterpret_cast<const float4*>(qrow + 4 * c);
+            const float4 hi = *reinterpret_cast<const float4*>(qrow + 32 + 4 * c);
+            const float l4[4] = {lo.x, lo.y, lo.z, lo.w}, h4[4] = {hi.x, hi.y, hi.z, hi.w};
+            if constexpr (ROT != 0) {
+                const int64_t prow = min(pos0 + r, p.table_len - 1);
+                const float4 cs = *reinterpret_cast<const float4*>(p.cos_t + prow * 32 + 4 * c);
+                const float4 sn = *reinterpret_cast<const float4*>(p.sin_t + prow * 32 + 4 * c);
+                const float c4[4] = {cs.x, cs.y, cs.z, cs.w}, s4[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rope_pair_scaled(l4[k], h4[k], c4[k], s4[k], p.scale, a[k], b[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    a[k] = l4[k] * p.scale;
+                    b[k] = h4[k] * p.scale;
+                }
+            }
+        }
+        *reinterpret_cast<float4*>(&Qs[r * LDS_STRIDE + 4 * c]) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4*>(&Qs[r * LDS_STRIDE + 32 + 4 * c]) = make_float4(b[0], b[1], b[2], b[3]);
+    }
+}
+
+// A lane's Q slice from a staged block (stage_q): row j, dims 16hh .. 16hh+15 and
+// 32+16hh .. 32+16hh+15 in contraction order (dim_group), as load_q gives it.
+__device__ __forceinline__ void read_q(float (&qreg)[32], const float* Qs, int j, int hh) {
+    const float* qr = &Qs[j * LDS_STRIDE + hh * 16];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 x = *reinterpret_cast<const float4*>(qr + dim_group(m));
+        qreg[4 * m + 0] = x.x;
+        qreg[4 * m + 1] = x.y;
+        qreg[4 * m + 2] = x.z;
+        qreg[4 * m + 3] = x.w;
     }
 }
 
@@ -748,6 +807,10 @@ void fwd_split_kernel(FwdParams p) {
     // per wave: K rows then V rows of its current tile; after the loop, its partial result
     __shared__ __attribute__((aligned(16))) float lds[kSplitWaves][2 * TBN * LDS_STRIDE];
     static_assert(34 * 64 <= 2 * TBN * LDS_STRIDE, "a wave's partial result fits its region");
+    // the block's 32 query rows, loaded once for all W waves (each wave used to load the same
+    // rows itself, with every lane of a load on its own cache line: about half of the heaviest
+    // blocks' start-up time on the 1142-token causal sequence)
+    __shared__ __attribute__((aligned(16))) float Qs[32 * LDS_STRIDE];
 
     const int tix = blockIdx.x / p.nunits;
     const int head = blockIdx.x - tix * p.nunits;
@@ -865,8 +928,10 @@ void fwd_split_kernel(FwdParams p) {
     if (t0 < t1) {
         KATTN_SPLIT_FETCH(t0)
     }
+    stage_q<ROT, 64 * W>(Qs, p, static_cast<int64_t>(lo + q0), head, off + q0, min(32, n - q0));
+    __syncthreads();
     float qreg[32];
-    load_q<ROT>(qreg, p, static_cast<int64_t>(lo + qi), head, pq, hh, qi < n);
+    read_q(qreg, Qs, j, hh);
     f32x16 O0, O1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -874,9 +939,15 @@ void fwd_split_kernel(FwdParams p) {
         O1[r] = 0.0f;
     }
     float m_run = kNegBig, l_run = 0.0f;
+    // Tile kt is in LDS while the next tile's rows are on their way into registers: they are
+    // requested as soon as the previous tile is staged, so they have a whole tile's work to
+    // arrive (requested between the scores and the P.V instead, they had half of it).
     if (t0 < t1) {
         KATTN_SPLIT_STASH()
         wave_sync_lds();
+        if (t0 + TBN < t1) {
+            KATTN_SPLIT_FETCH(t0 + TBN)
+        }
     }
     for (int kt = t0; kt < t1; kt += TBN) {
         const int klast = kt + TBN - 1;
@@ -889,18 +960,18 @@ void fwd_split_kernel(FwdParams p) {
             any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
             full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
         }
-        // the next tile's rows are requested between the scores and the P.V product
         f32x16 S0, S1;
-        if (any)
+        if (any) {
             tile_scores<false, true>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
-        if (kt + TBN < t1) {
-            KATTN_SPLIT_FETCH(kt + TBN)
+            tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         }
-        if (any) tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         wave_sync_lds();  // this wave is done with the tile
         if (kt + TBN < t1) {
             KATTN_SPLIT_STASH()
             wave_sync_lds();
+            if (kt + 2 * TBN < t1) {
+                KATTN_SPLIT_FETCH(kt + 2 * TBN)
+            }
         }
     }
 #undef KATTN_SPLIT_FETCH
