@@ -65,6 +65,7 @@ constexpr int BN = 64;        // key-range granularity of the planner's work est
 constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: exp2 of (-1e30 - m) is 0, never NaN
+constexpr float kRefSlack = 5.5451774f;  // 8 ln 2: how far a score max may pass the reference
 constexpr int kPlanThreads = 256;
 constexpr int kPlanBins = 1024;   // key-tile-count buckets (a multiple of kPlanThreads)
 
@@ -282,6 +283,31 @@ struct KeyInterval {
     int lo;
     unsigned span;
 };
+// Which key tiles [kt, klast] a wave of queries at positions pa .. plast (all of them live)
+// sees at all (any: kt <= any_hi and klast >= any_lo) and sees whole (full: kt >= full_lo and
+// klast <= full_hi): keys below nk, at most the query's position when causal, within hw of it
+// with a window.  The bounds are wave-uniform and computed once, so the per-tile tests are four
+// scalar compares.  A wave with no live query sees no tile.
+struct TileBounds {
+    int any_lo, any_hi, full_lo, full_hi;
+};
+__device__ inline TileBounds tile_bounds(bool live, int nk, int pa, int plast, int causal, int hw) {
+    int64_t any_hi = nk - 1, full_hi = nk - 1, any_lo = INT32_MIN, full_lo = INT32_MIN;
+    if (causal) {
+        any_hi = min(any_hi, static_cast<int64_t>(plast));
+        full_hi = min(full_hi, static_cast<int64_t>(pa));
+    }
+    if (hw >= 0) {
+        any_hi = min(any_hi, static_cast<int64_t>(plast) + hw);
+        any_lo = static_cast<int64_t>(pa) - hw;
+        full_lo = static_cast<int64_t>(plast) - hw;
+        full_hi = min(full_hi, static_cast<int64_t>(pa) + hw);
+    }
+    if (!live) any_hi = full_hi = INT32_MIN;
+    return {static_cast<int>(max(any_lo, static_cast<int64_t>(INT32_MIN))), static_cast<int>(any_hi),
+            static_cast<int>(max(full_lo, static_cast<int64_t>(INT32_MIN))), static_cast<int>(full_hi)};
+}
+
 __device__ inline KeyInterval visible_keys(int pq, int nk, int causal, int hw) {
     int lo = 0, hi = nk - 1;
     if (causal) hi = min(hi, pq);
@@ -314,13 +340,20 @@ __host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16
 
 // One tile's online-softmax update for the 32 queries of a wave (column j of lane j and
 // j + 32): S^T = K Q^T on FP32 MFMA from the staged K rows, the boundary mask when the tile
-// is not fully visible (masked scores become -inf, the same as skipping them), the running
-// max and sum, and O^T += V^T P^T from the staged V rows.  TWO: a 64-key tile (two 32-key
+// is not fully visible (masked scores become -inf, the same as skipping them), the exponent
+// reference and sum, and O^T += V^T P^T from the staged V rows.  TWO: a 64-key tile (two 32-key
 // score blocks).
-// tile_scores is the part up to the P.V product (scores, mask, running max and sum, rescale of
-// O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue loads between
-// the two.
-template <bool TWO, bool SKIP = TWO>
+// tile_scores is the part up to the P.V product (scores, mask, exponent reference and sum,
+// rescale of O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue
+// loads between the two.
+// m_run is the reference the exponentials are taken against, not the exact running max: a
+// query's reference moves to its tile max (and its l and O are rescaled by e^(old - new)) only
+// when that max exceeds the reference by more than kRefSlack.  Softmax is unchanged by a
+// common shift of one query's scores and O / l cancels the reference, so only the rounding
+// differs from a reference that tracks the max; every p stays at most e^kRefSlack = 256 and l
+// at most 256 per key.  Over a long row the reference settles after the first tile, and the
+// rescale (32 multiplies, one exponential) stops being paid on most tiles.
+template <bool TWO>
 __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
                                             f32x16& S1, f32x16& O0, f32x16& O1, float& m_run,
                                             float& l_run, bool full, int kt, KeyInterval vis,
@@ -376,10 +409,23 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
     }
     mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-    const float ml = m_new * kLog2e;
-    m_run = m_new;
+    // Only the lanes whose max crossed the slack move their reference (the others take
+    // alpha = 2^0 = 1 exactly), so a query's result never depends on the other queries of its
+    // wave.  A masked-out lane has mx = -inf and never moves; the first visible tile always does
+    // (m_run starts at kNegBig), and alpha is then 0 on l = O = 0.
+    const bool move = mx > m_run + kRefSlack;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            O0[r] *= alpha;
+            O1[r] *= alpha;
+        }
+    }
+    const float ml = m_run * kLog2e;
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -390,18 +436,7 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
             psum += S1[r];
         }
     }
-    l_run = l_run * alpha + psum;
-    // SKIP: over long key ranges (64-key tiles of global and causal rows, the key-split kernel's
-    // runs) the running max rarely moves after the first tiles, so the rescale is skipped when it
-    // moved in no lane (alpha is then exactly 1, so the result is unchanged).  On the short
-    // rows of a sliding window the test measured slower than the multiplies.
-    if (!SKIP || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            O0[r] *= alpha;
-            O1[r] *= alpha;
-        }
-    }
+    l_run += psum;
 }
 
 template <bool TWO>
@@ -595,7 +630,7 @@ template <int HPW, int QW, int TBN, int ROT, bool F16>
 __global__ __launch_bounds__(64 * HPW * QW) __attribute__((amdgpu_waves_per_eu(fwd_waves<TBN, ROT>())))
 void fwd_kernel(FwdParams p) {
     static_assert(TBN == 32 || TBN == 64, "tiles hold one or two 32-key score blocks");
-    constexpr bool ROPE_Q = ROT != 0, ROPE_K = ROT == 1;
+    constexpr bool ROPE_K = ROT == 1;
     constexpr int NT = 64 * HPW * QW;
     constexpr int BM = 32 * QW;
     constexpr bool TWO = TBN == 64;
@@ -629,7 +664,7 @@ void fwd_kernel(FwdParams p) {
         O0[r] = 0.0f;
         O1[r] = 0.0f;
     }
-    float m_run = kNegBig;  // running max of this lane's query
+    float m_run = kNegBig;  // exponent reference of this lane's query (lags the max by <= kRefSlack)
     float l_run = 0.0f;     // running sum over this lane half's keys
 
     int kbeg, kend;
@@ -733,20 +768,13 @@ void fwd_kernel(FwdParams p) {
 
     KATTN_STASH()
     __syncthreads();
+    const TileBounds tb = tile_bounds(wave_live, nk, pa, plast_w, p.causal, p.hw);
     for (int kt = kbeg; kt < kend; kt += TBN) {
 
         // Does this wave see some key of the tile, and does it see every one of them?
         const int klast = kt + TBN - 1;
-        bool any = wave_live && kt < nk;
-        bool full = wave_live && klast < nk;
-        if (p.causal) {
-            any = any && kt <= plast_w;
-            full = full && klast <= pa;
-        }
-        if (p.hw >= 0) {
-            any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
-            full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
-        }
+        const bool any = kt <= tb.any_hi && klast >= tb.any_lo;
+        const bool full = kt >= tb.full_lo && klast <= tb.full_hi;
         // The next tile's rows (the last trip re-reads this tile's, which are in cache) are
         // requested between the scores and the P.V product: the P.V half covers their latency,
         // and their registers are not held through the score MFMAs.
@@ -949,20 +977,14 @@ void fwd_split_kernel(FwdParams p) {
             KATTN_SPLIT_FETCH(t0 + TBN)
         }
     }
+    const TileBounds tb = tile_bounds(true, nk, pa, plast_w, p.causal, p.hw);
     for (int kt = t0; kt < t1; kt += TBN) {
         const int klast = kt + TBN - 1;
-        bool any = kt < nk, full = klast < nk;
-        if (p.causal) {
-            any = any && kt <= plast_w;
-            full = full && klast <= pa;
-        }
-        if (p.hw >= 0) {
-            any = any && kt <= plast_w + p.hw && klast >= pa - p.hw;
-            full = full && kt >= plast_w - p.hw && klast <= pa + p.hw;
-        }
+        const bool any = kt <= tb.any_hi && klast >= tb.any_lo;
+        const bool full = kt >= tb.full_lo && klast <= tb.full_hi;
         f32x16 S0, S1;
         if (any) {
-            tile_scores<false, true>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+            tile_scores<false>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
             tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         }
         wave_sync_lds();  // this wave is done with the tile
@@ -1362,12 +1384,14 @@ Shape pick_shape(int R, bool fused_banded) {
 // 32-key tiles for sliding windows (less waste over a band) and for keys from a cache; 64-key
 // tiles otherwise, causal included (two independent score chains per MFMA round: 2 % faster on
 // long causal sequences, 1.4 % with the fused rotation).
+// The two-wave shape serves only fused sliding-window launches, so it has no 64-key form.
 template <int HPW, int QW, int ROT, bool F16>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t stream) {
-    if (p.hw >= 0 || ROT == 2)
+    constexpr bool kOnly32 = ROT == 2 || (HPW == 1 && QW == 2);  // cache keys: always causal
+    if (kOnly32 || p.hw >= 0)
         hipLaunchKernelGGL((fwd_kernel<HPW, QW, 32, ROT, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
-    else if constexpr (ROT != 2)  // keys from a cache are always causal
+    else if constexpr (!kOnly32)
         hipLaunchKernelGGL((fwd_kernel<HPW, QW, 64, ROT, F16>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * HPW * QW), 0, stream, p);
 }
