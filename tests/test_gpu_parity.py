@@ -225,6 +225,79 @@ def test_each_sequence_alone_is_bit_identical_to_its_rows_in_the_batch(monkeypat
                 assert torch.equal(got, packed[lo:lo + n])
 
 
+# ----------------------------------------------------------------------------- large and shifted scores
+
+def _attention_only(case):
+    """GPU attention on q, k taken as already rotated, against the oracle without rotation."""
+    run = PrefillRun(case)
+    run.attention()
+    torch.cuda.synchronize()
+    ref = oracle.varlen_attention(case.q, case.k, case.v, case.cu, case.H, case.G, case.window,
+                                  case.causal, tables=None, threads=16)
+    return run.out.cpu().numpy(), ref
+
+
+def _score_bar(case):
+    """The output bar for scores larger than those of N(0,1) inputs: FP32 scores carry an
+    absolute error that grows with their magnitude (about 2^-24 of the partial sums per
+    accumulation step), so ATOL, set for scores of magnitude about 4, scales with the largest
+    |q.k| / 8 over the pairs of each sequence."""
+    H, G, R = case.H, case.G, case.H // case.G
+    smax = 0.0
+    for s in range(case.S):
+        lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+        if hi == lo:
+            continue
+        q = case.q[lo:hi].reshape(hi - lo, H, D).astype(np.float64)
+        k = case.k[lo:hi].reshape(hi - lo, G, D).astype(np.float64)
+        for h in range(H):
+            smax = max(smax, float(np.max(np.abs(q[:, h] @ k[:, h // R].T))) / 8.0)
+    return ATOL * max(1.0, smax / 4.0)
+
+
+def _set_score_shift(case, q_coef, k_of_pos):
+    """Dim 0 of every q head is set to q_coef[row] and dim 0 of every k head to k_of_pos(p) at
+    in-sequence position p, so each score gains q_coef * k_of_pos(p) / 8; the other dims stay
+    N(0,1)."""
+    for g in range(case.G):
+        for s in range(case.S):
+            lo, hi = int(case.cu[s]), int(case.cu[s + 1])
+            case.k[lo:hi, g * D] = k_of_pos(np.arange(hi - lo, dtype=np.float64)).astype(np.float32)
+    for h in range(case.H):
+        case.q[:, h * D] = q_coef
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (40, False), (17, True)])
+def test_score_ramps_move_the_reference(prefill_kernel, window, causal):
+    # Scores that rise (or fall) by about 1/8 per key position: along a 300-key row the max
+    # climbs about 54 base-2 units, so every kernel moves its exponent references up several
+    # times and rescales l and O; rows with coefficient -1 start at their max; 0 adds nothing.
+    lengths = [1, 37, 300, 129, 64]
+    case = wl.make_prefill(lengths, 4, 2, packed=True, window=window, causal=causal, seed=41)
+    rng = np.random.default_rng(41)
+    coef = rng.choice(np.array([1.0, -1.0, 0.5, 0.0], np.float32), size=case.T)
+    _set_score_shift(case, coef, lambda pos: pos)
+    got, ref = _attention_only(case)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, ref) <= _score_bar(case)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (40, False)])
+def test_scores_far_from_zero_move_the_reference(prefill_kernel, window, causal):
+    # A constant shift of -75 (coefficient 1) or +75 (coefficient -1) per row: the reference
+    # moves down below -64 base-2 units or up past +16 at the first visible tile; rows with
+    # coefficient 0 keep it at 0, so one wave mixes moved and unmoved lanes.  The shift is the
+    # same for every key of a row, so the softmax equals that of the unshifted scores.
+    lengths = [1, 37, 300, 129, 64]
+    case = wl.make_prefill(lengths, 4, 2, packed=True, window=window, causal=causal, seed=43)
+    rng = np.random.default_rng(43)
+    coef = rng.choice(np.array([1.0, -1.0, 0.0], np.float32), size=case.T)
+    _set_score_shift(case, coef, lambda pos: np.full(pos.shape, -600.0))
+    got, ref = _attention_only(case)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, ref) <= _score_bar(case)
+
+
 def test_gqa_matches_mha_with_repeated_kv():
     H, G = 9, 3
     case = wl.make_prefill([100, 257], H, G, packed=False, causal=True, seed=8)

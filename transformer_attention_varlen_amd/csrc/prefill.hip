@@ -20,8 +20,8 @@
 //   S^T = K Q^T, with v_mfma_f32_32x32x2f32: A = 32 keys x 2 dims (LDS), B =
 //   2 dims x 32 queries (registers).  In the 32x32 result lane l holds query
 //   column l%32 and 16 key rows, so the row max over keys is 15 in-lane
-//   maxima plus one v_permlane32_swap with lane l^32, and the running max,
-//   sum and the rescale of O are per lane.
+//   maxima plus one v_permlane32_swap with lane l^32, and the exponent
+//   reference, sum and the rescale of O are per lane.
 // * O^T = V^T P^T with the same instruction: the B operand P^T (2 keys x 32
 //   queries) is exactly register r of the score block -- keys 8(r/4)+(r%4)
 //   in lanes 0-31 and that +4 in lanes 32-63 -- so P never leaves registers;
@@ -31,8 +31,10 @@
 //   members of its RoPE pairs (q rotates in-lane), its Q slice is two
 //   64-byte runs and K is read as ds_read_b128.  V is read as float2 (dims
 //   2j, 2j+1) feeding two accumulators, so output dim d = 2i + block.
-// * scale is folded into q as it is loaded: exact for 1/8 (argus text.rs
-//   module docs).  exp is v_exp_f32 on (s - m) * log2(e).
+// * scale * log2(e) is folded into q as it is loaded (the pages fold the exact
+//   1/8, argus text.rs module docs; the extra factor costs one rounding per
+//   q element), so scores come out of the MFMA in base-2 exponent units and
+//   p = v_exp_f32(s - ref), with the subtraction skipped while ref is 0.
 // * Key tiles outside a query block's window / causal range are never
 //   loaded (never computed, per wave); tiles inside it skip the per-element
 //   mask, and only boundary tiles set masked scores to -inf -- which gives
@@ -64,8 +66,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BN = 64;        // key-range granularity of the planner's work estimate
 constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;  // running-max start: exp2 of (-1e30 - m) is 0, never NaN
-constexpr float kRefSlack = 5.5451774f;  // 8 ln 2: how far a score max may pass the reference
+constexpr float kNegBig = -1.0e30f;  // "no reference": exp2 of (-1e30 - m) is 0, never NaN
+// Exponent reference bounds, in base-2 units: a tile max more than kRefUp above a query's
+// reference moves it up (so every p is at most 2^16), and a row max that stays more than
+// -kRefDown below it moves it down (so the largest p of a row is at least 2^-64 and l never
+// underflows).
+constexpr float kRefUp = 16.0f;
+constexpr float kRefDown = -64.0f;
 constexpr int kPlanThreads = 256;
 constexpr int kPlanBins = 1024;   // key-tile-count buckets (a multiple of kPlanThreads)
 
@@ -256,7 +263,7 @@ struct FwdParams {
     int T, H, R, nunits, hw, causal;
     int nseq;  // sequences in the batch (S); the sliding-window kernel holds cu[0..S] in LDS
     int bm;    // query rows per tile-list item (used when tiles is NULL)
-    float scale;
+    float scale;  // the score scale times log2 e, folded into q as it is loaded
 };
 
 // The work item tix: from the planner's list, or, for a batch of one sequence (tiles == NULL),
@@ -346,18 +353,19 @@ __host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16
 // tile_scores is the part up to the P.V product (scores, mask, exponent reference and sum,
 // rescale of O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue
 // loads between the two.
-// m_run is the reference the exponentials are taken against, not the exact running max: a
-// query's reference moves to its tile max (and its l and O are rescaled by e^(old - new)) only
-// when that max exceeds the reference by more than kRefSlack.  Softmax is unchanged by a
-// common shift of one query's scores and O / l cancels the reference, so only the rounding
-// differs from a reference that tracks the max; every p stays at most e^kRefSlack = 256 and l
-// at most 256 per key.  Over a long row the reference settles after the first tile, and the
-// rescale (32 multiplies, one exponential) stops being paid on most tiles.
+// Scores are in base-2 units (q carries scale * log2 e) and p = 2^(s - ref).  ref is a
+// per-query exponent reference, not the running max: it starts at 0 and moves to the row max so
+// far (and that query's l and O are rescaled by 2^(old - new)) only when a tile max passes it by
+// more than kRefUp, or when the row max so far (seen, relative to ref) lies below kRefDown.
+// Softmax is unchanged by a common shift of one query's scores and O / l cancels the
+// reference, so only the rounding differs from the exact-max form.  With scores of ordinary
+// size no reference ever moves, and p = 2^s takes no subtraction; the rescale (32 multiplies,
+// one exponential) runs only on the tiles where some lane's reference moves.
 template <bool TWO>
 __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
-                                            f32x16& S1, f32x16& O0, f32x16& O1, float& m_run,
-                                            float& l_run, bool full, int kt, KeyInterval vis,
-                                            int j, int hh) {
+                                            f32x16& S1, f32x16& O0, f32x16& O1, float& ref,
+                                            float& seen, float& l_run, bool full, int kt,
+                                            KeyInterval vis, int j, int hh) {
     // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -408,16 +416,18 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
     }
-    mx = halves_max(mx);
-    // Only the lanes whose max crossed the slack move their reference (the others take
-    // alpha = 2^0 = 1 exactly), so a query's result never depends on the other queries of its
-    // wave.  A masked-out lane has mx = -inf and never moves; the first visible tile always does
-    // (m_run starts at kNegBig), and alpha is then 0 on l = O = 0.
-    const bool move = mx > m_run + kRefSlack;
+    mx = halves_max(mx) - ref;  // this tile's max relative to the reference (-inf: no key)
+    seen = fmaxf(seen, mx);
+    // Only the lanes that cross a bound move their reference (the others take alpha = 2^0 = 1
+    // exactly), so a query's result never depends on the other queries of its wave.  The move is
+    // to the row max so far: up when this tile passes kRefUp (seen = mx then), down when a
+    // visible tile leaves the row max below kRefDown.
+    const bool move = (mx > kRefUp) | ((seen < kRefDown) & (mx != -INFINITY));  // no branches
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float m_new = move ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-        m_run = m_new;
+        const float ref_new = move ? ref + seen : ref;
+        const float alpha = __builtin_amdgcn_exp2f(ref - ref_new);
+        seen = move ? 0.0f : seen;
+        ref = ref_new;
         l_run *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -425,15 +435,26 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
             O1[r] *= alpha;
         }
     }
-    const float ml = m_run * kLog2e;
     float psum = 0.0f;
+    if (__builtin_amdgcn_ballot_w64(ref != 0.0f) == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        S0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[r], kLog2e, -ml));
-        psum += S0[r];
-        if constexpr (TWO) {
-            S1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[r], kLog2e, -ml));
-            psum += S1[r];
+        for (int r = 0; r < 16; ++r) {
+            S0[r] = __builtin_amdgcn_exp2f(S0[r]);
+            psum += S0[r];
+            if constexpr (TWO) {
+                S1[r] = __builtin_amdgcn_exp2f(S1[r]);
+                psum += S1[r];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            S0[r] = __builtin_amdgcn_exp2f(S0[r] - ref);
+            psum += S0[r];
+            if constexpr (TWO) {
+                S1[r] = __builtin_amdgcn_exp2f(S1[r] - ref);
+                psum += S1[r];
+            }
         }
     }
     l_run += psum;
@@ -463,10 +484,10 @@ __device__ __forceinline__ void tile_pv(const float* Vs, const f32x16& S0, const
 template <bool TWO>
 __device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
                                             const float (&qreg)[32], f32x16& O0, f32x16& O1,
-                                            float& m_run, float& l_run, bool full, int kt,
-                                            KeyInterval vis, int j, int hh) {
+                                            float& ref, float& seen, float& l_run, bool full,
+                                            int kt, KeyInterval vis, int j, int hh) {
     f32x16 S0, S1;
-    tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+    tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
     tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 }
 
@@ -664,8 +685,9 @@ void fwd_kernel(FwdParams p) {
         O0[r] = 0.0f;
         O1[r] = 0.0f;
     }
-    float m_run = kNegBig;  // exponent reference of this lane's query (lags the max by <= kRefSlack)
-    float l_run = 0.0f;     // running sum over this lane half's keys
+    float ref = 0.0f;        // exponent reference of this lane's query
+    float seen = -INFINITY;  // its row max so far, relative to ref
+    float l_run = 0.0f;      // running sum over this lane half's keys
 
     int kbeg, kend;
     key_range(off + q0, off + min(q0 + BM, n), nk, p.hw, p.causal, kbeg, kend);
@@ -779,7 +801,7 @@ void fwd_kernel(FwdParams p) {
         // requested between the scores and the P.V product: the P.V half covers their latency,
         // and their registers are not held through the score MFMAs.
         f32x16 S0, S1;
-        if (any) tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+        if (any) tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
         KATTN_FETCH(min(kt + TBN, kend - 1))
         if (any) tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 
@@ -966,7 +988,7 @@ void fwd_split_kernel(FwdParams p) {
         O0[r] = 0.0f;
         O1[r] = 0.0f;
     }
-    float m_run = kNegBig, l_run = 0.0f;
+    float ref = 0.0f, seen = -INFINITY, l_run = 0.0f;
     // Tile kt is in LDS while the next tile's rows are on their way into registers: they are
     // requested as soon as the previous tile is staged, so they have a whole tile's work to
     // arrive (requested between the scores and the P.V instead, they had half of it).
@@ -984,7 +1006,7 @@ void fwd_split_kernel(FwdParams p) {
         const bool full = kt >= tb.full_lo && klast <= tb.full_hi;
         f32x16 S0, S1;
         if (any) {
-            tile_scores<false>(Ks, qreg, S0, S1, O0, O1, m_run, l_run, full, kt, vis, j, hh);
+            tile_scores<false>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
             tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         }
         wave_sync_lds();  // this wave is done with the tile
@@ -1008,7 +1030,9 @@ void fwd_split_kernel(FwdParams p) {
         mine[r * 64 + lane] = O0[r];
         mine[(16 + r) * 64 + lane] = O1[r];
     }
-    mine[32 * 64 + lane] = m_run;
+    // a wave that saw no key of this query (l = 0) takes no part in the common reference M: its
+    // reference would stay 0 while the others' may have moved far below it
+    mine[32 * 64 + lane] = halves_sum(l_run) > 0.0f ? ref : kNegBig;
     mine[33 * 64 + lane] = l_run;
     __syncthreads();
     if (qi >= n) return;
@@ -1026,7 +1050,7 @@ void fwd_split_kernel(FwdParams p) {
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
         const float* part = lds[w];
-        const float f = __builtin_amdgcn_exp2f((part[32 * 64 + lane] - M) * kLog2e);
+        const float f = __builtin_amdgcn_exp2f(part[32 * 64 + lane] - M);
         l_tot = __builtin_fmaf(part[33 * 64 + lane] + part[33 * 64 + (lane ^ 32)], f, l_tot);
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
@@ -1299,7 +1323,7 @@ void band_kernel(FwdParams p) {
                 O0[k] = 0.0f;
                 O1[k] = 0.0f;
             }
-            float m_run = kNegBig, l_run = 0.0f;
+            float ref = 0.0f, seen = -INFINITY, l_run = 0.0f;
             // unrolled: the compiler schedules across the five steps (1 % on the two-pass form)
 #pragma unroll
             for (int s = 0; s < kBandSteps; ++s) {
@@ -1322,7 +1346,7 @@ void band_kernel(FwdParams p) {
                 const int slot = (t - tbase) & (kBandSlots - 1);
                 f32x16 S0, S1;
                 if (any)
-                    tile_scores<false>(Ks[slot], qreg, S0, S1, O0, O1, m_run, l_run, full, k0,
+                    tile_scores<false>(Ks[slot], qreg, S0, S1, O0, O1, ref, seen, l_run, full, k0,
                                        vis, j, hh);
                 if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
                 if (any) tile_pv<false>(Vs[slot], S0, S1, O0, O1, j, hh);
@@ -1624,7 +1648,7 @@ int varlen_fwd(const char* fn, void* out, int64_t out_stride, const float* q, in
     p.nunits = nunits;
     p.hw = hw;
     p.causal = causal;
-    p.scale = scale;
+    p.scale = scale * kLog2e;  // scores in base-2 exponent units
     p.nseq = S;
     if (band) {
         // a persistent grid of up to kBandWorkGroupsPerCU per CU: each head's query blocks cut
@@ -1811,7 +1835,7 @@ extern "C" int kattn_prefill_cached(float* out, int64_t out_stride, const float*
     p.nunits = nunits;
     p.hw = -1;
     p.causal = 1;
-    p.scale = scale;
+    p.scale = scale * kLog2e;  // scores in base-2 exponent units
     p.nseq = B;
     if (gm.split) {
         if (cos != nullptr) launch_split<2, false>(p, grid, gm.wide, stream);
