@@ -67,12 +67,10 @@ constexpr int BN = 64;        // key-range granularity of the planner's work est
 constexpr int LDS_STRIDE = 68;  // floats per staged row: 64 + 4 pad, conflict-free b128 reads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // "no reference": exp2 of (-1e30 - m) is 0, never NaN
-// Exponent reference bounds, in base-2 units: a tile max more than kRefUp above a query's
-// reference moves it up (so every p is at most 2^16), and a row max that stays more than
-// -kRefDown below it moves it down (so the largest p of a row is at least 2^-64 and l never
-// underflows).
-constexpr float kRefUp = 16.0f;
-constexpr float kRefDown = -64.0f;
+// Exponent reference bounds (tile_scores): a query keeps its reference while a tile's sum of
+// p = 2^(s - ref) stays at most 2^16 and its running sum reaches 2^-64.
+constexpr float kTileSumMax = 65536.0f;
+constexpr float kSumMin = 5.42101086e-20f;  // 2^-64
 constexpr int kPlanThreads = 256;
 constexpr int kPlanBins = 1024;   // key-tile-count buckets (a multiple of kPlanThreads)
 
@@ -353,20 +351,12 @@ __host__ __device__ constexpr int dim_group(int m) { return 4 * m + (m >= 4 ? 16
 // tile_scores is the part up to the P.V product (scores, mask, exponent reference and sum,
 // rescale of O), leaving S0 (and S1) holding P^T; tile_pv is the product.  A kernel may issue
 // loads between the two.
-// Scores are in base-2 units (q carries scale * log2 e) and p = 2^(s - ref).  ref is a
-// per-query exponent reference, not the running max: it starts at 0 and moves to the row max so
-// far (and that query's l and O are rescaled by 2^(old - new)) only when a tile max passes it by
-// more than kRefUp, or when the row max so far (seen, relative to ref) lies below kRefDown.
-// Softmax is unchanged by a common shift of one query's scores and O / l cancels the
-// reference, so only the rounding differs from the exact-max form.  With scores of ordinary
-// size no reference ever moves, and p = 2^s takes no subtraction; the rescale (32 multiplies,
-// one exponential) runs only on the tiles where some lane's reference moves.
+
+// S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1).  Scores are in
+// base-2 exponent units: q carries scale * log2 e.
 template <bool TWO>
-__device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
-                                            f32x16& S1, f32x16& O0, f32x16& O1, float& ref,
-                                            float& seen, float& l_run, bool full, int kt,
-                                            KeyInterval vis, int j, int hh) {
-    // S^T = K Q^T for keys kt..kt+31 (S0) and, with 64-key tiles, kt+32..kt+63 (S1)
+__device__ __forceinline__ void tile_score_mfma(const float* Ks, const float (&qreg)[32],
+                                                f32x16& S0, f32x16& S1, int j, int hh) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         S0[r] = 0.0f;
@@ -394,51 +384,36 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
             S1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, qreg[4 * m + 3], S1, 0, 0, 0);
         }
     }
-
     __builtin_amdgcn_s_setprio(0);
-    if (!full) {
-        // boundary tile: masked scores become -inf (the same as skipping them); score r holds
-        // key kt + 8(r/4) + 4hh + (r%4), and S1 the key 32 above it
-        const int x = kt + 4 * hh - vis.lo;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d0 = x + 8 * (r >> 2) + (r & 3);
-            if (static_cast<unsigned>(d0) > vis.span) S0[r] = -INFINITY;
-            if (TWO && static_cast<unsigned>(d0 + 32) > vis.span) S1[r] = -INFINITY;
-        }
-    }
+}
 
-    // online softmax
-    float mx = S0[0];
+// Boundary tile: masked scores become -inf (the same as skipping them); score r holds key
+// kt + 8(r/4) + 4hh + (r%4), and S1 the key 32 above it.
+template <bool TWO>
+__device__ __forceinline__ void tile_mask(f32x16& S0, f32x16& S1, int kt, KeyInterval vis, int hh) {
+    const int x = kt + 4 * hh - vis.lo;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
-    if constexpr (TWO) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+    for (int r = 0; r < 16; ++r) {
+        const int d0 = x + 8 * (r >> 2) + (r & 3);
+        if (static_cast<unsigned>(d0) > vis.span) S0[r] = -INFINITY;
+        if (TWO && static_cast<unsigned>(d0 + 32) > vis.span) S1[r] = -INFINITY;
     }
-    mx = halves_max(mx) - ref;  // this tile's max relative to the reference (-inf: no key)
-    seen = fmaxf(seen, mx);
-    // Only the lanes that cross a bound move their reference (the others take alpha = 2^0 = 1
-    // exactly), so a query's result never depends on the other queries of its wave.  The move is
-    // to the row max so far: up when this tile passes kRefUp (seen = mx then), down when a
-    // visible tile leaves the row max below kRefDown.
-    const bool move = (mx > kRefUp) | ((seen < kRefDown) & (mx != -INFINITY));  // no branches
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float ref_new = move ? ref + seen : ref;
-        const float alpha = __builtin_amdgcn_exp2f(ref - ref_new);
-        seen = move ? 0.0f : seen;
-        ref = ref_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            O0[r] *= alpha;
-            O1[r] *= alpha;
-        }
-    }
-    float psum = 0.0f;
+}
+
+// p = 2^(s - ref) in place (no subtraction while no lane of the wave has moved its reference
+// from 0); returns the query's sum over the tile (both lane halves).
+template <bool TWO>
+__device__ __forceinline__ float tile_exp(f32x16& S0, f32x16& S1, float ref) {
+    float psum;
     if (__builtin_amdgcn_ballot_w64(ref != 0.0f) == 0) {
+        S0[0] = __builtin_amdgcn_exp2f(S0[0]);
+        psum = S0[0];
+        if constexpr (TWO) {
+            S1[0] = __builtin_amdgcn_exp2f(S1[0]);
+            psum += S1[0];
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 1; r < 16; ++r) {
             S0[r] = __builtin_amdgcn_exp2f(S0[r]);
             psum += S0[r];
             if constexpr (TWO) {
@@ -447,8 +422,14 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
             }
         }
     } else {
+        S0[0] = __builtin_amdgcn_exp2f(S0[0] - ref);
+        psum = S0[0];
+        if constexpr (TWO) {
+            S1[0] = __builtin_amdgcn_exp2f(S1[0] - ref);
+            psum += S1[0];
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 1; r < 16; ++r) {
             S0[r] = __builtin_amdgcn_exp2f(S0[r] - ref);
             psum += S0[r];
             if constexpr (TWO) {
@@ -457,7 +438,62 @@ __device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)
             }
         }
     }
-    l_run += psum;
+    return halves_sum(psum);
+}
+
+// ref is a per-query exponent reference (p = 2^(s - ref)), not the running max, and l is the
+// query's running sum (the same in both lane halves).  ref starts at 0 and is kept while the
+// tile's sum t stays at most kTileSumMax (so every p is at most 2^16) and l + t reaches
+// kSumMin (so the row's mass never underflows); a query that breaks either bound on a tile
+// where it sees some key moves ref to that tile's max score, and its l and O are rescaled by
+// 2^(old - new).  The test looks only at the query's own values, so its bits never depend on
+// the other queries of its wave.  Softmax is unchanged by a common shift of one query's
+// scores and O / l cancels the reference, so only the rounding differs from the exact-max
+// form.  With scores of ordinary size no reference ever moves: a tile costs the exponentials
+// and their sum, with no max and no subtraction.  When some lane must move, the wave scores
+// the tile again (K is still staged) to find the max.
+template <bool TWO>
+__device__ __forceinline__ void tile_scores(const float* Ks, const float (&qreg)[32], f32x16& S0,
+                                            f32x16& S1, f32x16& O0, f32x16& O1, float& ref,
+                                            float& l, bool full, int kt, KeyInterval vis, int j,
+                                            int hh) {
+    tile_score_mfma<TWO>(Ks, qreg, S0, S1, j, hh);
+    bool sees = true;  // does this lane's query see some key of the tile?
+    if (!full) {
+        tile_mask<TWO>(S0, S1, kt, vis, hh);
+        const int first = max(kt, vis.lo);
+        sees = first <= kt + (TWO ? 63 : 31) &&
+               static_cast<unsigned>(first - vis.lo) <= vis.span;
+    }
+    float t = tile_exp<TWO>(S0, S1, ref);
+    // !(a <= b) also catches an infinite or NaN sum
+    const bool move = sees && !(t <= kTileSumMax && l + t >= kSumMin);
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        tile_score_mfma<TWO>(Ks, qreg, S0, S1, j, hh);
+        if (!full) tile_mask<TWO>(S0, S1, kt, vis, hh);
+        float mx = S0[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S0[r]);
+        if constexpr (TWO) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S1[r]);
+        }
+        mx = halves_max(mx);  // finite where the lane sees a key
+        // l is 0 (and O is 0) until the query's first visible key, and at least 2^-64 after
+        // it, so a move with l > 0 is a move up (alpha <= 2^-10); a move down happens only on the
+        // first visible tile, where scaling is skipped (2^(ref - ref_new) may overflow there)
+        const float ref_new = move ? mx : ref;
+        const float alpha = l > 0.0f ? __builtin_amdgcn_exp2f(ref - ref_new) : 1.0f;
+        ref = ref_new;
+        l *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            O0[r] *= alpha;
+            O1[r] *= alpha;
+        }
+        t = tile_exp<TWO>(S0, S1, ref);
+    }
+    l += t;
 }
 
 template <bool TWO>
@@ -479,16 +515,6 @@ __device__ __forceinline__ void tile_pv(const float* Vs, const f32x16& S0, const
         }
     }
     __builtin_amdgcn_s_setprio(0);
-}
-
-template <bool TWO>
-__device__ __forceinline__ void tile_update(const float* Ks, const float* Vs,
-                                            const float (&qreg)[32], f32x16& O0, f32x16& O1,
-                                            float& ref, float& seen, float& l_run, bool full,
-                                            int kt, KeyInterval vis, int j, int hh) {
-    f32x16 S0, S1;
-    tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
-    tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 }
 
 // TBN: keys per K/V tile.  Global launches use 64-key tiles (two 32-key score blocks per MFMA
@@ -685,9 +711,8 @@ void fwd_kernel(FwdParams p) {
         O0[r] = 0.0f;
         O1[r] = 0.0f;
     }
-    float ref = 0.0f;        // exponent reference of this lane's query
-    float seen = -INFINITY;  // its row max so far, relative to ref
-    float l_run = 0.0f;      // running sum over this lane half's keys
+    float ref = 0.0f;  // exponent reference of this lane's query
+    float l = 0.0f;    // its running sum (the same in both lane halves)
 
     int kbeg, kend;
     key_range(off + q0, off + min(q0 + BM, n), nk, p.hw, p.causal, kbeg, kend);
@@ -801,7 +826,7 @@ void fwd_kernel(FwdParams p) {
         // requested between the scores and the P.V product: the P.V half covers their latency,
         // and their registers are not held through the score MFMAs.
         f32x16 S0, S1;
-        if (any) tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
+        if (any) tile_scores<TWO>(Ks, qreg, S0, S1, O0, O1, ref, l, full, kt, vis, j, hh);
         KATTN_FETCH(min(kt + TBN, kend - 1))
         if (any) tile_pv<TWO>(Vs, S0, S1, O0, O1, j, hh);
 
@@ -813,9 +838,8 @@ void fwd_kernel(FwdParams p) {
 #undef KATTN_FETCH_ROW
 #undef KATTN_STASH
 
-    const float l_tot = halves_sum(l_run);
     if (qi < n) {
-        const float inv = 1.0f / l_tot;
+        const float inv = 1.0f / l;
         const int64_t at = static_cast<int64_t>(lo + qi) * p.out_stride + head * kHeadDim;
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
@@ -842,7 +866,7 @@ void fwd_kernel(FwdParams p) {
 // region (wave-level synchronisation only), and the four partial results are merged through
 // LDS at the end with the log-sum-exp algebra: M = max m_w, l = sum l_w e^(m_w - M),
 // O = sum O_w e^(m_w - M) / l, wave w writing dims 16w .. 16w+15.  The per-tile math is the
-// main kernel's (tile_update).
+// main kernel's (tile_scores, tile_pv).
 constexpr int kSplitTBN = 32;
 
 // W waves per work-group (4, or 8 for launches of very few query tiles: the whole CU on one
@@ -988,7 +1012,7 @@ void fwd_split_kernel(FwdParams p) {
         O0[r] = 0.0f;
         O1[r] = 0.0f;
     }
-    float ref = 0.0f, seen = -INFINITY, l_run = 0.0f;
+    float ref = 0.0f, l = 0.0f;
     // Tile kt is in LDS while the next tile's rows are on their way into registers: they are
     // requested as soon as the previous tile is staged, so they have a whole tile's work to
     // arrive (requested between the scores and the P.V instead, they had half of it).
@@ -1006,7 +1030,7 @@ void fwd_split_kernel(FwdParams p) {
         const bool full = kt >= tb.full_lo && klast <= tb.full_hi;
         f32x16 S0, S1;
         if (any) {
-            tile_scores<false>(Ks, qreg, S0, S1, O0, O1, ref, seen, l_run, full, kt, vis, j, hh);
+            tile_scores<false>(Ks, qreg, S0, S1, O0, O1, ref, l, full, kt, vis, j, hh);
             tile_pv<false>(Vs, S0, S1, O0, O1, j, hh);
         }
         wave_sync_lds();  // this wave is done with the tile
@@ -1032,8 +1056,8 @@ void fwd_split_kernel(FwdParams p) {
     }
     // a wave that saw no key of this query (l = 0) takes no part in the common reference M: its
     // reference would stay 0 while the others' may have moved far below it
-    mine[32 * 64 + lane] = halves_sum(l_run) > 0.0f ? ref : kNegBig;
-    mine[33 * 64 + lane] = l_run;
+    mine[32 * 64 + lane] = l > 0.0f ? ref : kNegBig;
+    mine[33 * 64 + lane] = l;
     __syncthreads();
     if (qi >= n) return;
     float M = kNegBig;
@@ -1051,7 +1075,7 @@ void fwd_split_kernel(FwdParams p) {
     for (int w = 0; w < kSplitWaves; ++w) {
         const float* part = lds[w];
         const float f = __builtin_amdgcn_exp2f(part[32 * 64 + lane] - M);
-        l_tot = __builtin_fmaf(part[33 * 64 + lane] + part[33 * 64 + (lane ^ 32)], f, l_tot);
+        l_tot = __builtin_fmaf(part[33 * 64 + lane], f, l_tot);
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
             acc[2 * k] = __builtin_fmaf(part[(r0 + k) * 64 + lane], f, acc[2 * k]);
@@ -1323,7 +1347,7 @@ void band_kernel(FwdParams p) {
                 O0[k] = 0.0f;
                 O1[k] = 0.0f;
             }
-            float ref = 0.0f, seen = -INFINITY, l_run = 0.0f;
+            float ref = 0.0f, l = 0.0f;
             // unrolled: the compiler schedules across the five steps (1 % on the two-pass form)
 #pragma unroll
             for (int s = 0; s < kBandSteps; ++s) {
@@ -1346,7 +1370,7 @@ void band_kernel(FwdParams p) {
                 const int slot = (t - tbase) & (kBandSlots - 1);
                 f32x16 S0, S1;
                 if (any)
-                    tile_scores<false>(Ks[slot], qreg, S0, S1, O0, O1, ref, seen, l_run, full, k0,
+                    tile_scores<false>(Ks[slot], qreg, S0, S1, O0, O1, ref, l, full, k0,
                                        vis, j, hh);
                 if (fetch) { KATTN_BAND_FETCH(pk, pv, pt, 0, tn) }
                 if (any) tile_pv<false>(Vs[slot], S0, S1, O0, O1, j, hh);
@@ -1358,9 +1382,8 @@ void band_kernel(FwdParams p) {
                 }
             }
 
-            const float l_tot = halves_sum(l_run);
             if (qlive) {
-                const float inv = 1.0f / l_tot;
+                const float inv = 1.0f / l;
                 const int64_t at = static_cast<int64_t>(qrow) * p.out_stride + head * kHeadDim;
 #pragma unroll
                 for (int grp = 0; grp < 4; ++grp) {
