@@ -19,8 +19,8 @@
 // * One wave = 32 queries x 1 head.  Scores are computed transposed,
 //   S^T = K Q^T, with v_mfma_f32_32x32x2f32: A = 32 keys x 2 dims (LDS), B =
 //   2 dims x 32 queries (registers).  In the 32x32 result lane l holds query
-//   column l%32 and 16 key rows, so the row max over keys is 15 in-lane
-//   maxima plus one v_permlane32_swap with lane l^32, and the exponent
+//   column l%32 and 16 key rows, so a row reduction over keys is in-lane
+//   arithmetic plus one v_permlane32_swap with lane l^32, and the exponent
 //   reference, sum and the rescale of O are per lane.
 // * O^T = V^T P^T with the same instruction: the B operand P^T (2 keys x 32
 //   queries) is exactly register r of the score block -- keys 8(r/4)+(r%4)
