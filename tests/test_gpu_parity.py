@@ -298,6 +298,39 @@ def test_scores_far_from_zero_move_the_reference(prefill_kernel, window, causal)
     assert max_err(got, ref) <= _score_bar(case)
 
 
+def _norm_bar(q, k):
+    """ATOL scaled as in _score_bar, with the largest score bounded by the largest norms (the
+    rotation keeps each pair's norm, so the bound holds for rotated rows too)."""
+    qn = float(np.max(np.linalg.norm(q.reshape(-1, D).astype(np.float64), axis=1))) if q.size else 0.0
+    kn = float(np.max(np.linalg.norm(k.reshape(-1, D).astype(np.float64), axis=1))) if k.size else 0.0
+    return ATOL * max(1.0, qn * kn / 8.0 / 4.0)
+
+
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (40, False)])
+def test_large_scores_with_fused_rope(prefill_kernel, window, causal):
+    # q scaled by 8: scores of standard deviation about 8, so the row maxima pass the exponent
+    # references' upper bound in the fused-rotation kernels too
+    lengths = [1, 37, 300, 129, 64]
+    case = wl.make_prefill(lengths, 4, 2, packed=True, window=window, causal=causal, seed=47)
+    case.q[:] *= 8.0
+    run = PrefillRun(case)
+    run.step_fused()
+    torch.cuda.synchronize()
+    got = run.out.cpu().numpy()
+    ref = oracle_prefill(case)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, ref) <= _norm_bar(case.q, case.k)
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+def test_large_scores_from_a_cache(prefill_kernel, rotate):
+    # the chunked prefill's tile kernels (keys from a cache) with q scaled by 8
+    case = wl.make_chunked([1, 31, 32, 33, 129], [0, 0, 5, 100, 200], 9, 3, 400, seed=49)
+    case.q[:] *= 8.0
+    kk = np.concatenate([case.k.reshape(-1, D), case.k_cache.reshape(-1, D)], axis=0)
+    _check_chunk(case, rotate, atol=_norm_bar(case.q, kk))
+
+
 def test_gqa_matches_mha_with_repeated_kv():
     H, G = 9, 3
     case = wl.make_prefill([100, 257], H, G, packed=False, causal=True, seed=8)
@@ -533,7 +566,7 @@ def test_f16_output_local_layer_workload():
 from transformer_attention_varlen_amd.session import ChunkRun  # noqa: E402
 
 
-def _check_chunk(case, rotate, pad_rows=3):
+def _check_chunk(case, rotate, pad_rows=3, atol=ATOL):
     run = ChunkRun(case, rotate=rotate, out_pad_rows=pad_rows)
     run.out_full.fill_(float("nan"))
     run.step()
@@ -543,7 +576,7 @@ def _check_chunk(case, rotate, pad_rows=3):
                                         case.k_cache, case.v_cache, case.H, case.G, tables=tables,
                                         threads=16)
     got = run.out_full.cpu().numpy()
-    assert max_err(got[:case.T], ref) <= ATOL
+    assert max_err(got[:case.T], ref) <= atol
     assert np.all(np.isnan(got[case.T:]))  # rows past T are never written
     gk, gv = run.k_cache.cpu().numpy(), run.v_cache.cpu().numpy()
     for b in range(case.B):
