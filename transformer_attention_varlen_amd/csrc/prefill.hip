@@ -945,8 +945,7 @@ void fwd_split_kernel(FwdParams p) {
     v4 pk[2 * kRows], pv[2 * kRows], pt[2 * kRows];
     // Row addresses as in fwd_kernel: a tile inside the keys from its wave-uniform start plus
     // this lane's fixed offsets (no per-row 64-bit multiply on the vector ALU); a tile past the
-    // last key clamps each row to it.  With the rescale skip below, the 1142-token causal case
-    // went 29.8 -> 29.4 us.
+    // last key clamps each row to it.
     const int64_t koff0 = static_cast<int64_t>(srow) * p.k_stride;
     const int64_t voff0 = static_cast<int64_t>(srow) * p.v_stride;
     const int64_t kstep = 8 * p.k_stride;
