@@ -282,17 +282,20 @@ def test_score_ramps_move_the_reference(prefill_kernel, window, causal):
     assert max_err(got, ref) <= _score_bar(case)
 
 
+@pytest.mark.parametrize("shift", [75.0, 100.0])
 @pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (40, False)])
-def test_scores_far_from_zero_move_the_reference(prefill_kernel, window, causal):
-    # A constant shift of -75 (coefficient 1) or +75 (coefficient -1) per row: the reference
-    # moves down below -64 base-2 units or up past +16 at the first visible tile; rows with
-    # coefficient 0 keep it at 0, so one wave mixes moved and unmoved lanes.  The shift is the
-    # same for every key of a row, so the softmax equals that of the unshifted scores.
+def test_scores_far_from_zero_move_the_reference(prefill_kernel, window, causal, shift):
+    # A constant shift of -shift (coefficient 1) or +shift (coefficient -1) per row: the
+    # reference moves down below -64 base-2 units or up past +16 at the first visible tile; rows
+    # with coefficient 0 keep it at 0, so one wave mixes moved and unmoved lanes.  At +100 (144
+    # base-2 units) the first pass's exponentials overflow to infinity before the move.  The
+    # shift is the same for every key of a row, so the softmax equals that of the unshifted
+    # scores.
     lengths = [1, 37, 300, 129, 64]
     case = wl.make_prefill(lengths, 4, 2, packed=True, window=window, causal=causal, seed=43)
     rng = np.random.default_rng(43)
     coef = rng.choice(np.array([1.0, -1.0, 0.0], np.float32), size=case.T)
-    _set_score_shift(case, coef, lambda pos: np.full(pos.shape, -600.0))
+    _set_score_shift(case, coef, lambda pos: np.full(pos.shape, -8.0 * shift))
     got, ref = _attention_only(case)
     assert np.all(np.isfinite(got))
     assert max_err(got, ref) <= _score_bar(case)
