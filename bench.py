@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--preroll-ms", type=float, default=300.0,
                     help="after the warmup steps, further untimed steps until this much wall "
                          "time has passed, so the timed steps start at full clock (reported)")
+    ap.add_argument("--part-preroll-ms", type=float, default=100.0,
+                    help="before each part's timed calls, untimed calls of it (each after a cache "
+                         "flush) for this much wall time (reported per part)")
     ap.add_argument("--parts", default="1,2,3a,3b,3c,4,5",
                     help="comma list of extra workloads to time, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -109,12 +112,29 @@ def time_calls(torch, fn, steps, warmup, flush=None):
     return float(np.mean(times)), float(np.min(times))
 
 
-def prefill_part(torch, key, steps, warmup, flush):
+def preroll(torch, fn, flush, ms):
+    """Untimed calls of `fn` (each after a cache flush, as in the timed loop) until `ms` of wall
+    time have passed, so a part is timed at the clock its own work holds rather than the one the
+    previous part left.  Returns (calls, ms)."""
+    n = 0
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    while (time.perf_counter() - t) * 1e3 < ms:
+        if flush is not None:
+            flush()
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+    return {"calls": n, "ms": round((time.perf_counter() - t) * 1e3, 1)}
+
+
+def prefill_part(torch, key, steps, warmup, flush, preroll_ms=0.0):
     from transformer_attention_varlen_amd import metrics, workloads as wl
     from transformer_attention_varlen_amd.session import PrefillRun
     case = wl.build(key)
     run = PrefillRun(case)
     # fused first, on the unrotated inputs; then the prologue and the two-pass attention
+    pre = preroll(torch, run.attention_rope, flush, preroll_ms)
     fused_ms, _ = time_calls(torch, run.attention_rope, steps, warmup, flush)
     out16 = torch.empty((case.T, case.H * 64), dtype=torch.float16, device="cuda")
     f16_ms, _ = time_calls(torch, lambda: run.attention_f16(out16, fused=True),
@@ -138,18 +158,19 @@ def prefill_part(torch, key, steps, warmup, flush):
            "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1),
            "fused_rope_attn_ms": round(fused_ms, 4),
            "fused_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-           "fused_f16_out_ms": round(f16_ms, 4),
+           "fused_f16_out_ms": round(f16_ms, 4), "preroll": pre,
            "traffic": part_traffic(wl.WORKLOADS[key].name, "prefill.hip")}
     del run
     torch.cuda.empty_cache()
     return res
 
 
-def decode_part(torch, steps, warmup, flush):
+def decode_part(torch, steps, warmup, flush, preroll_ms=0.0):
     from transformer_attention_varlen_amd import metrics, workloads as wl
     from transformer_attention_varlen_amd.session import DecodeRun
     case = wl.build("4")
     run = DecodeRun(case, rotate=True)
+    pre = preroll(torch, run.step, flush, preroll_ms)
     mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
     median_ms = time_calls.median
     # a serving loop: steps back to back (no flush), wall clock over all of them, after a few
@@ -197,7 +218,7 @@ def decode_part(torch, steps, warmup, flush):
            "flushed_loop_ms": round(flushed_ms, 4),
            "flushed_loop_frac_hbm": round(nbytes / (flushed_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "flushed_loop_how": f"{n_fl} (flush, step) pairs less {n_fl} flushes, wall clock",
-           "graph_replay_ms": round(graph_ms, 4),
+           "graph_replay_ms": round(graph_ms, 4), "preroll": pre,
            "algorithmic_mb": round(nbytes / 1e6, 2), "gbs": round(gbs, 1),
            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "traffic": part_traffic(wl.WORKLOADS["4"].name, "decode.hip")}
@@ -206,12 +227,13 @@ def decode_part(torch, steps, warmup, flush):
     return res
 
 
-def chunk_part(torch, steps, warmup, flush):
+def chunk_part(torch, steps, warmup, flush, preroll_ms=0.0):
     from transformer_attention_varlen_amd import metrics, workloads as wl
     from transformer_attention_varlen_amd.session import ChunkRun
     case = wl.build("5")
     run = ChunkRun(case, rotate=True)
     # every call appends the same chunk at the same rows, so repeated calls do equal work
+    pre = preroll(torch, run.step, flush, preroll_ms)
     mean_ms, min_ms = time_calls(torch, run.step, steps, warmup, flush)
     median_ms = time_calls.median
     flops = metrics.chunk_flops(case.lengths, case.offsets, case.H)
@@ -221,7 +243,7 @@ def chunk_part(torch, steps, warmup, flush):
            "ms": round(mean_ms, 4), "ms_min": round(min_ms, 4), "ms_median": round(median_ms, 4),
            "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
            "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
-           "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4)}
+           "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4), "preroll": pre}
     del run
     torch.cuda.empty_cache()
     return res
@@ -542,13 +564,14 @@ def main():
         flush = Flusher(torch)
         for k in keys:
             psteps, pwarm = max(5, args.steps // 2), 2
+            pms = args.part_preroll_ms
             if k == "4":
-                parts[PARTS[k]] = decode_part(torch, max(psteps, 20), pwarm, flush)
+                parts[PARTS[k]] = decode_part(torch, max(psteps, 20), pwarm, flush, pms)
             elif k == "5":
-                parts[PARTS[k]] = chunk_part(torch, psteps, pwarm, flush)
+                parts[PARTS[k]] = chunk_part(torch, psteps, pwarm, flush, pms)
             else:
                 parts[PARTS[k]] = prefill_part(torch, k, max(3, psteps // 4) if k == "2" else psteps,
-                                               pwarm, flush)
+                                               pwarm, flush, pms)
         del flush
     out["parts"] = parts
     out["ceilings"] = measure_ceilings(torch) if args.parts != "none" else None
