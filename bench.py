@@ -128,6 +128,22 @@ def preroll(torch, fn, flush, ms):
     return {"calls": n, "ms": round((time.perf_counter() - t) * 1e3, 1)}
 
 
+def flushed_loop_ms(torch, fn, flush, n):
+    """Per call with the caches flushed before it, without an event pair around it: a loop of n
+    (flush, call) pairs less a loop of n flushes alone, both queued with no host wait inside
+    (the flush reads 1 GiB, so the host stays ahead of the GPU), wall clock."""
+    def loop_wall(f):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    pair_ms = loop_wall(lambda: (flush(), fn()))
+    return pair_ms - loop_wall(flush)
+
+
 def prefill_part(torch, key, steps, warmup, flush, preroll_ms=0.0):
     from transformer_attention_varlen_amd import metrics, workloads as wl
     from transformer_attention_varlen_amd.session import PrefillRun
@@ -143,6 +159,8 @@ def prefill_part(torch, key, steps, warmup, flush, preroll_ms=0.0):
     run.rope()
     mean_ms, min_ms = time_calls(torch, run.attention, steps, warmup, flush)
     median_ms = time_calls.median
+    # the same call without the event pair (which adds a few us to a call of tens of us)
+    loop_ms = flushed_loop_ms(torch, run.attention, flush, max(steps, 100))
     rope_ms, _ = time_calls(torch, run.rope, max(3, steps // 4), 1, flush)
     flops = metrics.prefill_flops(case.lengths, case.H, case.window, case.causal)
     tflops = flops / (mean_ms * 1e-3) / 1e12
@@ -154,6 +172,9 @@ def prefill_part(torch, key, steps, warmup, flush, preroll_ms=0.0):
            "mtok_s": round(case.T / (mean_ms * 1e-3) / 1e6, 3),
            "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tflops, 2),
            "frac_fp32_mfma": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+           "flushed_loop_ms": round(loop_ms, 4),
+           "flushed_loop_frac_fp32_mfma": round(flops / (loop_ms * 1e-3) / 1e12
+                                                / PEAK_FP32_MFMA_TFLOPS, 4),
            "rope_ms": round(rope_ms, 4),
            "rope_gbs": round(rb / (rope_ms * 1e-3) / 1e9, 1),
            "fused_rope_attn_ms": round(fused_ms, 4),
@@ -184,22 +205,8 @@ def decode_part(torch, steps, warmup, flush, preroll_ms=0.0):
         run.step()
     torch.cuda.synchronize()
     loop_ms = (time.perf_counter() - t) * 1e3 / loop_steps
-    # per call with the caches flushed before it, without an event pair around it: a loop of
-    # (flush, step) pairs less a loop of flushes alone, both queued with no host wait inside
-    # (the flush reads 1 GiB, so the host stays ahead of the GPU)
     n_fl = max(steps, 100)
-
-    def loop_wall(fn):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n_fl):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n_fl
-
-    pair_ms = loop_wall(lambda: (flush(), run.step()))
-    flush_ms = loop_wall(flush)
-    flushed_ms = pair_ms - flush_ms
+    flushed_ms = flushed_loop_ms(torch, run.step, flush, n_fl)
     # the same step captured once in a HIP graph and replayed (fixed shape, device counts)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
