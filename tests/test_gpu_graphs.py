@@ -42,10 +42,13 @@ def _padded_cu(lengths, S_cap):
     return cu
 
 
+@pytest.mark.parametrize("S_cap", [8, 1])
 @pytest.mark.parametrize("H,G,window,causal,theta", [(9, 3, -1, True, 1e5),
                                                      (12, 12, 128, False, 1e4)])
-def test_fused_prefill_graph_replays_with_new_batches(H, G, window, causal, theta):
-    S_cap, T_cap = 8, 2048
+def test_fused_prefill_graph_replays_with_new_batches(H, G, window, causal, theta, S_cap):
+    # S_cap = 1: a one-sequence bucket (no planning launch: the tile kernel reads its blocks'
+    # bounds from cu on every replay)
+    T_cap = 2048
     rng = np.random.default_rng(71)
     q = torch.zeros((T_cap, H * D), device="cuda")
     k = torch.zeros((T_cap, G * D), device="cuda")

@@ -197,6 +197,50 @@ def test_window_of_twice_the_length_is_bit_identical_to_global(causal):
     assert torch.equal(ga, gb)
 
 
+@pytest.mark.parametrize("mode", [None, "4", "8"])
+@pytest.mark.parametrize("n,T,max_seqlen,causal,fused", [(300, 520, 520, True, False),
+                                                         (300, 520, 333, False, True),
+                                                         (37, 200, 200, True, True),
+                                                         (300, 520, 300, True, False)])
+def test_one_sequence_in_a_larger_bucket(monkeypatch, mode, n, T, max_seqlen, causal, fused):
+    # A batch of one sequence sized for a bucket: T and max_seqlen at or above the sequence's n
+    # rows, cu = {0, n}.  A one-sequence launch plans nothing on the device, so its blocks come
+    # from cu alone: rows past n are neither attended to nor written.
+    if mode is not None:
+        monkeypatch.setenv("KATTN_SPLIT", mode)
+    H, G, theta = 9, 3, 1e5
+    case = wl.make_prefill([n], H, G, packed=False, window=-1, causal=causal, theta=theta,
+                           seed=23)
+    rng = np.random.default_rng(24)
+
+    def padded(a):
+        extra = rng.standard_normal((T - n, a.shape[1]), dtype=np.float32)
+        return torch.from_numpy(np.concatenate([a, extra])).cuda()
+
+    q, k, v = padded(case.q), padded(case.k), padded(case.v)
+    cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    out = torch.full((T, H * 64), float("nan"), device="cuda")
+    ws = torch.empty(max(kattn.kattn_varlen_fwd_workspace(1, T), 256), dtype=torch.uint8,
+                     device="cuda")
+    tables = oracle.rope_tables(theta, max_seqlen)
+    if fused:
+        cos_h, sin_h = kattn.kattn_rope_tables(theta, max_seqlen)
+        kattn.kattn_varlen_fwd_rope(out, q, k, v, cu, 1, T, max_seqlen, H, G,
+                                    torch.from_numpy(cos_h).cuda(), torch.from_numpy(sin_h).cuda(),
+                                    causal=causal, workspace=ws)
+        ref = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, -1, causal,
+                                      tables=tables, threads=16)
+    else:
+        kattn.kattn_varlen_fwd(out, q, k, v, cu, 1, T, max_seqlen, H, G, causal=causal,
+                               workspace=ws)
+        ref = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, -1, causal,
+                                      tables=None, threads=16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[n:]))  # rows past the sequence are never written
+    assert max_err(got[:n], ref) <= ATOL
+
+
 @pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (20, False)])
 def test_each_sequence_alone_is_bit_identical_to_its_rows_in_the_batch(monkeypatch, window,
                                                                         causal):
