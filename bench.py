@@ -10,7 +10,10 @@ the in-place RoPE prologue (kattn_rope_prologue), then the attention forward
 fused form of the same step (kattn_varlen_fwd_rope, RoPE inside the tile
 loads) is timed beside it.  The same line carries the other workloads of the
 path, each timed per call with HIP events on the stream it runs on and the
-L2/MALL flushed between calls:
+L2/MALL flushed between calls, after a 100 ms pre-roll of its own untimed
+calls (the GPU idles while a part builds its inputs on the host, and the first
+calls after that run below full clock); the two-pass prefill attention and the
+decode step are also timed from a flushed loop without event pairs:
 
   prefill_local_w128    ModernBERT local layer, 64 x U[16,512], window 128
   prefill_global_long   the headline workload's fused and binary16-output forms
