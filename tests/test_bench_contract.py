@@ -49,5 +49,7 @@ def test_short_run_prints_one_json_line_with_the_contract_fields():
     assert ctx["masked_fill_ms_per_layer"]["value"] == 114.13
     assert ctx["kv_cat_ms_per_decode_token"]["value"] == 14.0
     dec = d["parts"]["decode_b64"]
-    assert dec["decode_ms"] > 0 and dec["back_to_back_ms"] > 0
+    assert dec["decode_ms"] > 0 and dec["back_to_back_ms"] > 0 and dec["flushed_loop_ms"] > 0
     assert 0 < dec["frac_hbm"] < 1 and 0 < dec["back_to_back_frac_hbm"] < 1
+    # each part is timed after a pre-roll of its own calls
+    assert dec["preroll"]["calls"] >= 1 and dec["preroll"]["ms"] >= 100.0
