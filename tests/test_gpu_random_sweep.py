@@ -3,7 +3,9 @@
 Each case draws its sequence lengths (empty and single-token sequences included), the q/kv
 head ratio, the window, the causal flag, the RoPE base and, for the cache paths, the cache
 size and fill, from a generator seeded by the case number, so a failure names a case that
-can be rerun alone.  The library picks its kernels by launch size as in production.
+can be rerun alone.  Every prefill case runs with the library's own kernel choice (by launch
+size, as in production) and again through each tile kernel forced with KATTN_SPLIT; the
+binary16-output cases draw the kernel with the case.
 """
 import numpy as np
 import pytest
@@ -40,8 +42,16 @@ def _lengths(rng, max_len):
     return lengths.astype(np.int32)
 
 
+# None: the library's own choice; the others force a tile kernel (KATTN_SPLIT): shared-tile,
+# key-split with 4 and 8 waves, sliding-window (where it applies; other launches keep their own)
+MODES = [None, "0", "4", "8", "band"]
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("seed", range(24))
-def test_random_prefill(seed):
+def test_random_prefill(monkeypatch, seed, mode):
+    if mode is not None:
+        monkeypatch.setenv("KATTN_SPLIT", mode)
     rng = np.random.default_rng(10_000 + seed)
     H, G = RATIOS[rng.integers(0, len(RATIOS))]
     lengths = _lengths(rng, 400)
@@ -63,6 +73,39 @@ def test_random_prefill(seed):
     ref = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, window, causal,
                                   tables=tables, threads=16)
     assert _err(got[:case.T], ref) <= ATOL, (H, G, lengths.tolist(), window, causal, fused)
+    assert np.all(np.isnan(got[case.T:]))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_f16_output(monkeypatch, seed):
+    # binary16 output: within half a binary16 ulp (at the larger magnitude) plus the FP32 bar of
+    # the oracle's FP64 result; the tile kernel drawn with the case
+    rng = np.random.default_rng(40_000 + seed)
+    mode = MODES[rng.integers(0, len(MODES))]
+    if mode is not None:
+        monkeypatch.setenv("KATTN_SPLIT", mode)
+    H, G = RATIOS[rng.integers(0, len(RATIOS))]
+    lengths = _lengths(rng, 300)
+    window = int(rng.choice([-1, -1, 5, 64, 128]))
+    causal = bool(rng.random() < 0.5)
+    theta = float(rng.choice([1e4, 1e5]))
+    fused = bool(rng.random() < 0.5)
+    case = wl.make_prefill(lengths, H, G, packed=(H == G and rng.random() < 0.5), window=window,
+                           causal=causal, theta=theta, seed=seed + 500)
+    run = PrefillRun(case)
+    out16 = torch.full((case.T + 2, H * 64), float("nan"), dtype=torch.float16, device="cuda")
+    if not fused:
+        run.rope()
+    run.attention_f16(out16[:case.T], fused=fused)
+    torch.cuda.synchronize()
+    got = out16.cpu().numpy()
+    tables = oracle.rope_tables(theta, max(case.max_seqlen, 1))
+    ref64 = oracle.varlen_attention(case.q, case.k, case.v, case.cu, H, G, window, causal,
+                                    tables=tables, threads=16, out_dtype=np.float64)
+    a = np.maximum(np.abs(ref64), np.abs(got[:case.T].astype(np.float64))).astype(np.float16)
+    bound = 0.5 * np.spacing(a).astype(np.float64) + ATOL
+    err = np.abs(got[:case.T].astype(np.float64) - ref64)
+    assert np.all(err <= bound), (mode, H, G, lengths.tolist(), window, causal, fused)
     assert np.all(np.isnan(got[case.T:]))
 
 
